@@ -1,0 +1,106 @@
+"""Brute-force check of the streaming call: full attention over the whole stream.
+
+Independent of the cache model in ``cache.py`` and of ``attention.attend``: it
+lays out every token of blocks 0..n, decides visibility of each key block by a
+predicate on (block id, query block id), places visible blocks at the times a
+training clip of the same visible length would give them, rotates with complex
+exponentials, and runs torch's scaled_dot_product_attention in float64 under
+an explicit boolean mask.  Meant for tiny workloads only.
+
+Sources: "Vidu S2 vs PixVerse R2" blog (orkas.ai), sections "What real-time
+changes" (each block sees only earlier blocks) and "Choice 3: bounded memory"
+(permanent first blocks, a window of recent blocks, positions kept inside the
+trained range).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+
+
+def visible_block(b: int, n: int, n_sink: int, n_window: int) -> bool:
+    """Is block b part of the context of query block n?"""
+    if b == n:
+        return True
+    if b > n:
+        return False                      # the future is never visible
+    if b < n_sink:
+        return True                       # sink blocks are pinned for good
+    return n_window > 0 and b >= n - n_window
+
+
+def start_times(n: int, w: synth.Workload):
+    """Start time of each visible block b <= n (dict), from the visible layout."""
+    vis = [b for b in range(n + 1) if visible_block(b, n, w.n_sink, w.n_window)]
+    n_s = sum(1 for b in vis if b < w.n_sink and b != n)
+    shift = -n_s * w.frames if w.policy == "relative" else 0
+    return {b: w.frames * sum(1 for c in vis if c < b) + shift for b in vis}
+
+
+def _pair_angles(t, h, wcol, head_dim, theta):
+    p_all = head_dim // 2
+    ph = pw = p_all // 3
+    pt = p_all - ph - pw
+    out = np.empty(t.shape + (p_all,), dtype=np.float64)
+    for p in range(p_all):
+        if p < pt:
+            out[..., p] = t * theta ** (-p / pt)
+        elif p < pt + ph:
+            out[..., p] = h * theta ** (-(p - pt) / ph)
+        else:
+            out[..., p] = wcol * theta ** (-(p - pt - ph) / pw)
+    return out
+
+
+def _rope_complex(x, t, h, wcol, theta):
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    z = z * np.exp(1j * _pair_angles(t, h, wcol, x.shape[-1], theta))
+    y = np.empty_like(x)
+    y[..., 0::2], y[..., 1::2] = z.real, z.imag
+    return y
+
+
+def chunk(w: synth.Workload, n: int, s: int, seed: int = 0, contents=None):
+    """(O [B, H, d], LSE [H, B]) of query block n at step s, by brute force."""
+    B, H, d = w.shape
+    tok = np.arange(B)
+    f = tok // (w.lat_h * w.lat_w)
+    hh = (tok // w.lat_w) % w.lat_h
+    wc = tok % w.lat_w
+    times = start_times(n, w)
+    q_st, k_cur, v_cur = synth.qkv(w, n, s, seed)
+    ks, vs, key_block = [], [], []
+    for b in range(n + 1):
+        if b == n:
+            k_st, v_st = k_cur, v_cur
+        else:
+            kind = "noisy" if (w.twin and s < w.n_steps) else "clean"
+            if contents is not None:
+                k_st, v_st = contents(b, kind)
+            elif kind == "clean":
+                k_st, v_st = synth.committed_kv(w, b, seed)
+            else:
+                k_st, v_st = synth.noisy_kv(w, b, seed)
+        t0 = times.get(b, 0)
+        ks.append(_rope_complex(synth.as_f64(w, k_st), (t0 + f)[:, None], hh[:, None], wc[:, None],
+                                w.rope_theta))
+        vs.append(synth.as_f64(w, v_st))
+        key_block.append(np.full(B, b))
+    q = _rope_complex(synth.as_f64(w, q_st), (times[n] + f)[:, None], hh[:, None], wc[:, None],
+                      w.rope_theta)
+    k = np.concatenate(ks, 0)
+    v = np.concatenate(vs, 0)
+    kb = np.concatenate(key_block)
+    allowed = np.array([visible_block(int(b), n, w.n_sink, w.n_window) for b in kb])
+    mask = torch.from_numpy(np.broadcast_to(allowed, (B, kb.size)).copy())
+    qt = torch.from_numpy(q).permute(1, 0, 2)          # [H, B, d]
+    kt = torch.from_numpy(k).permute(1, 0, 2)
+    vt = torch.from_numpy(v).permute(1, 0, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    # LSE from the same masked scores, for the normaliser check
+    sc = (qt @ kt.transpose(1, 2)) / np.sqrt(d)
+    sc = sc.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(sc, dim=-1)
+    return o.permute(1, 0, 2).numpy(), lse.numpy()
