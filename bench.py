@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of streaming block-causal chunk attention on one MI355X.
+
+A step is one chunk of the 540p dense stream in steady state (full window,
+eviction every chunk): for each of the 4 denoising steps, append the current
+block's K/V (fused RoPE + append kernel) and attend its queries over
+[sink, 3 window blocks, current] (bf16 MFMA attention kernel); then evict the
+oldest window block and commit the current one (index remaps).  Inputs are
+seeded synthetic N(0,1)*0.5 bf16 tensors of the workload's shapes, resident in
+HBM before timing.
+
+Prints ONE JSON line.  `value` = attention TFLOP per chunk / wall time per
+chunk (everything in the step counted in the time).  `roofline` is the
+attention kernel alone (HIP events on the launch stream), against the bf16
+dense MFMA peak.  `cpu_baseline` times the fp64 oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
+PEAK_HBM_GBPS = 8000.0
+
+WORKLOADS = {"c2": 2, "c3": 3, "c4": 4, "c5": 5}
+
+
+def attn_flops(B, H, d, n_keys):
+    return 4.0 * B * n_keys * d * H
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("attend.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "streaming_block_causal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(ROOT, "profiles", f"attend_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, sample_heads):
+    """Time the fp64 oracle on `sample_heads` heads (all rows) of one steady-state call."""
+    from threadpoolctl import threadpool_info
+
+    import oracle.stream as ostream
+    n = w.n_sink + w.n_window + 1
+    st = ostream.Stream(w)
+    st.slot_inputs(n, 1)                          # warm the input cache (draws are not the oracle)
+    t0 = time.perf_counter()
+    st.call(n, 1, heads=list(range(sample_heads)))
+    dt = time.perf_counter() - t0
+    keys = (w.n_sink + w.n_window + 1) * w.block_tokens
+    flops = attn_flops(w.block_tokens, sample_heads, w.head_dim, keys)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"one steady-state call (chunk {n}, step 1), {sample_heads} of {w.n_heads} heads, "
+                      f"all {w.block_tokens} queries x {keys} keys, fp64 numpy; {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed chunks")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed chunks")
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the chunk attention path has no multi-GPU sharding "
+              "in this build (heads would shard across GPUs; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from streaming_block_causal_amd.cache import Cache, CacheConfig
+
+    w = synth.WORKLOADS[WORKLOADS[args.workload]]
+    cfg = CacheConfig(n_heads=w.n_heads, head_dim=w.head_dim, frames_per_block=w.frames, lat_h=w.lat_h,
+                      lat_w=w.lat_w, n_sink=w.n_sink, n_window=w.n_window, twin=w.twin,
+                      sparse=w.sparse_keep is not None, dtype=w.dtype, rope_theta=w.rope_theta,
+                      policy=w.policy)
+    dev = "cuda"
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    cache = Cache(cfg, device=dev, stream=stream)
+    B, H, d, T = w.block_tokens, w.n_heads, w.head_dim, w.n_steps
+    shape = (B, H, d)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+
+    def draw():
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * w.scale).to(torch.bfloat16)
+
+    # two input sets (alternating chunks), resident in HBM before timing
+    sets = [[(draw(), draw(), draw()) for _ in range(T)] for _ in range(2)]
+    noisy = [(draw(), draw()) for _ in range(2)]
+    out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    nt = -(-B // 128)
+
+    n_slots_full = w.n_sink + w.n_window + 1
+    state = {"block": 0, "window": 0, "sinks": 0}
+
+    def commit():
+        b = state["block"]
+        if state["sinks"] >= w.n_sink and w.n_window > 0 and state["window"] == w.n_window:
+            cache.evict()
+            state["window"] -= 1
+        cache.append("clean", None, None, b)
+        if state["sinks"] < w.n_sink:
+            state["sinks"] += 1
+        else:
+            state["window"] += 1
+        if w.twin:
+            kn, vn = noisy[b % 2]
+            cache.append("noisy", kn, vn, b)
+        state["block"] += 1
+
+    ev = {"attn": [], "append": []}
+    last_mask = {}
+
+    def chunk(record):
+        b = state["block"]
+        for s in range(T):
+            q, k, v = sets[b % 2][s]
+            if record:
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record(stream)
+            cache.append("current", k, v, b)
+            if record:
+                e1.record(stream)
+            step = "final" if s == T - 1 else "intermediate"
+            if w.sparse_keep is not None:
+                idx, k_row = cache.build_tile_mask(q, w.sparse_keep)
+                last_mask["idx"] = idx
+                cache.attend(q, step, tile_idx=idx, k_row=k_row, out=out)
+            else:
+                cache.attend(q, step, out=out)
+            if record:
+                e2.record(stream)
+                ev["append"].append((e0, e1))
+                ev["attn"].append((e1, e2))
+        commit()
+
+    # fill the cache to steady state, then warm up
+    while state["block"] < n_slots_full - 1:
+        chunk(False)
+    for _ in range(args.warmup):
+        chunk(False)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        chunk(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    attn_ms = [a.elapsed_time(b) for a, b in ev["attn"]]
+    app_ms = [a.elapsed_time(b) for a, b in ev["append"]]
+    keys = n_slots_full * B
+    if w.sparse_keep is None:
+        flops_call = attn_flops(B, H, d, keys)
+    else:
+        # exact kept-tile work of the last mask: sum of valid_q * valid_k over kept tile pairs
+        idx = last_mask["idx"].long()
+        valid = torch.clamp(B - 128 * torch.arange(nt, device=dev), max=128).double()
+        vk = valid[idx % nt]                                   # [H, nt, k_row]
+        flops_call = float(4.0 * d * (vk.sum(dim=2) * valid[None, :]).sum().item())
+    flops_chunk = flops_call * T
+    ms_chunk = dt / args.steps * 1e3
+    avg_attn = sum(attn_ms) / len(attn_ms)
+    achieved = flops_call / (avg_attn * 1e-3) / 1e12
+    append_bytes = 2 * 2 * B * H * d * 2          # read raw K,V + write K,V (bf16)
+    avg_app = sum(app_ms) / len(app_ms)
+    res = {
+        "metric": "chunk-attention TFLOP/s (sink+window KV, 540p dense bf16, whole chunk step)",
+        "value": flops_chunk / (ms_chunk * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_chunk,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "block_tokens": B, "keys": keys, "heads": H, "head_dim": d,
+                   "n_sink": w.n_sink, "n_window": w.n_window, "steps_per_chunk": T,
+                   "latent_grid": [w.frames, w.lat_h, w.lat_w], "parallelism": "single GPU"},
+        "latent_frames_per_s": w.frames / (ms_chunk * 1e-3),
+        "frac_of_bf16_peak_step": flops_chunk / (ms_chunk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "attention_ms_per_call": avg_attn,
+        "append_ms_per_call": avg_app,
+        "append_gbps": append_bytes / (avg_app * 1e-3) / 1e9,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(args.workload),
+                     "kernel": "attend_bf16_kernel<false>", "flops_per_launch": flops_call},
+    }
+    if args.cpu_heads > 0:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

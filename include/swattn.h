@@ -1,0 +1,197 @@
+/*
+ * swattn.h -- C ABI of the streaming block-causal chunk-attention library
+ * (libswattn.so, HIP kernels for AMD gfx950 / MI355X).
+ *
+ * The method (sources cited by page title and section):
+ *  - Video is generated block by block in time order; a block sees only earlier
+ *    content, and a denoising step of the current block attends to the cached
+ *    history plus itself ("Vidu S2 vs PixVerse R2" blog, orkas.ai, section
+ *    "What real-time changes"; Vidu S2 paper read, yingwang.github.io,
+ *    section 2.2 on block-wise causal attention).
+ *  - The history is bounded: the first blocks stay as permanent sinks, a
+ *    sliding window keeps the most recent blocks, the rest is dropped; RoPE
+ *    positions are relocated (S1) or made relative in time (R2) so they stay
+ *    inside the trained range (blog, section "Choice 3: bounded memory").
+ *  - TwinCache: each history block is kept as a noisy and a clean copy;
+ *    intermediate denoising steps read the noisy copy, the final step the clean
+ *    one (blog, section "Choice 3: bounded memory").
+ *  - Block-sparse attention skips most key tiles (blog, section "Choice 4: where
+ *    the speed comes from", >90% sparsity).
+ *
+ * Conventions for every call
+ *  - Tensor arguments are DEVICE pointers (hipMalloc'd or torch CUDA storage),
+ *    contiguous, owned by the caller, and must stay alive until the work
+ *    enqueued on the cache's stream has finished.
+ *  - Raw Q/K/V of a block are token-major [B][H][d]: token index in
+ *    (frame, row, column) row-major order, B = frames * lat_h * lat_w, in the
+ *    cache dtype (bf16 stored as raw 16-bit patterns, or fp32).
+ *  - GPU work is enqueued asynchronously on the stream given at create; cache
+ *    metadata (which block sits where, time bases) is updated synchronously on
+ *    the host.  No call blocks on the GPU except create and read-back calls.
+ *  - Every call validates its arguments and the cache state before enqueuing
+ *    anything; on error it returns a status != SW_OK, leaves the cache state
+ *    unchanged and sets a thread-local message readable by sw_last_error().
+ *  - A handle is not thread-safe; use one handle per thread or serialise.
+ *  - No call allocates device memory: the caller passes one device pool of
+ *    sw_cache_required_bytes() bytes at create, which the library carves.
+ *  - A handle created with device_pool == NULL and pool_bytes == 0 is
+ *    metadata-only: append / evict / relocate / inspect behave as usual but
+ *    touch no device (any pointers passed are only checked for NULL); calls that
+ *    would launch a kernel return SW_ERR_STATE.  It lets hosts without a GPU
+ *    test the cache bookkeeping.
+ */
+#ifndef SWATTN_H
+#define SWATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sw_cache sw_cache; /* opaque, library-owned host handle */
+
+typedef enum {
+  SW_OK = 0,
+  SW_ERR_INVALID_ARG = 1, /* NULL pointer, out-of-range value */
+  SW_ERR_SHAPE = 2,       /* configuration the kernels do not support in size */
+  SW_ERR_STATE = 3,       /* call not allowed in the current cache state */
+  SW_ERR_CAPACITY = 4,    /* pool too small, window full, mask buffer too small */
+  SW_ERR_UNSUPPORTED = 5, /* dtype / head_dim / variant combination not built */
+  SW_ERR_HIP = 6          /* a HIP runtime call failed (message has the HIP error) */
+} sw_status;
+
+typedef enum { SW_BF16 = 0, SW_F32 = 1 } sw_dtype;
+
+/* What an append writes.
+ *  SW_KV_CURRENT: the current (not yet committed) block's K/V for this
+ *                 denoising step; overwrites the staged current block.
+ *  SW_KV_CLEAN:   commit a block to the history.  With k_raw == v_raw == NULL
+ *                 the staged current block is promoted (no bytes move); with
+ *                 pointers, those raw K/V are written as the committed block
+ *                 (used to rebuild a cache, e.g. on resume).
+ *  SW_KV_NOISY:   (TwinCache only) the noisy copy of the block just committed. */
+typedef enum { SW_KV_CURRENT = 0, SW_KV_CLEAN = 1, SW_KV_NOISY = 2 } sw_kv_kind;
+
+/* Which TwinCache copy of the history a denoising step reads (blog, "Choice 3"):
+ * intermediate steps read the noisy copies, the final step the clean ones.
+ * Without TwinCache both read the single (clean) copy. */
+typedef enum { SW_STEP_INTERMEDIATE = 0, SW_STEP_FINAL = 1 } sw_step_kind;
+
+/* Time base of logical slot l of the materialised sequence
+ * [sinks..., window oldest->newest..., current], F = frames per block:
+ *  SW_ROPE_S1_RELOCATE:   base_l = l * F.
+ *  SW_ROPE_RELATIVE_TIME: window j -> j * F, current -> n_window_used * F,
+ *                         sink i -> (i - n_sinks_used) * F.
+ * Both keep every position inside [-S*F, (S+W+1)*F) however long the stream
+ * runs (blog, "Choice 3": S1 RoPE relocation, R2 relative-time RoPE). */
+typedef enum { SW_ROPE_S1_RELOCATE = 0, SW_ROPE_RELATIVE_TIME = 1 } sw_rope_policy;
+
+typedef struct {
+  int32_t n_heads;          /* H >= 1 */
+  int32_t head_dim;         /* d: 128 (bf16 or fp32) or 64 (fp32) */
+  int32_t frames_per_block; /* F >= 1 */
+  int32_t lat_h, lat_w;     /* latent grid of a frame; B = F*lat_h*lat_w <= 65536 */
+  int32_t n_sink;           /* S >= 0 */
+  int32_t n_window;         /* W >= 0; S + W + 1 <= 16 */
+  int32_t twin;             /* 0 | 1: keep noisy + clean copies of history blocks */
+  int32_t sparse;           /* 0 | 1: keep pooled key-tile means for sw_build_tile_mask (bf16 only) */
+  sw_dtype dtype;           /* storage and input dtype */
+  double rope_theta;        /* RoPE base, > 1 (10000 is the usual value) */
+  sw_rope_policy policy;    /* initial relocation policy */
+  int32_t tile;             /* block-sparse tile edge; must be 128 */
+} sw_cache_config;
+
+/* RoPE layout (pages name 3D RoPE over (t, h, w) without details -- Vidu S2
+ * paper read, abbreviation table): P = d/2 pairs, pair p rotates dims
+ * (2p, 2p+1); time gets P - 2*floor(P/3) pairs, then height and width
+ * floor(P/3) each; inside an axis with P_a pairs, pair j turns by
+ * pos * theta^(-j/P_a). */
+
+typedef struct {
+  int32_t role;          /* 0 sink, 1 window, 2 current */
+  int64_t block_id;
+  int32_t physical_slot; /* ring slot holding the block (changes with eviction) */
+  int32_t time_base;     /* RoPE time of the block's first frame */
+  int32_t twin_complete; /* 1 if the noisy copy exists (always 1 without TwinCache) */
+} sw_slot_info;
+
+/* Thread-local message of the last failed call ("" if none). */
+const char* sw_last_error(void);
+
+/* Device bytes the cache needs for `cfg` (K/V slots, twin copies, pooled
+ * key means, RoPE tables).  Host-only; no device call. */
+sw_status sw_cache_required_bytes(const sw_cache_config* cfg, size_t* bytes);
+
+/* Create a cache in `device_pool` (pool_bytes >= required, 256-byte aligned).
+ * hip_stream: a hipStream_t (NULL = the default stream).  Uploads the RoPE
+ * tables (a blocking copy) and zeroes the pool.  *out receives the handle. */
+sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t pool_bytes,
+                          void* hip_stream, sw_cache** out);
+
+/* Free the host handle.  The caller frees the pool after the stream drains. */
+sw_status sw_cache_destroy(sw_cache* c);
+
+/* Append a block's raw K/V [B][H][d] (see sw_kv_kind).  The kernel rotates K
+ * at block-local positions (t = frame, h, w), stores V, both head-major, and
+ * (sparse caches) the per-128-token-tile means of the rotated K.
+ * Rules: block ids of commits strictly increase; CURRENT may be re-appended
+ * each step with the same id; CLEAN into a full window returns
+ * SW_ERR_CAPACITY (evict first); with TwinCache the call after a CLEAN must be
+ * the NOISY append of the same block id (else SW_ERR_STATE). */
+sw_status sw_cache_append_block(sw_cache* c, sw_kv_kind kind, const void* k_raw,
+                                const void* v_raw, int64_t block_id);
+
+/* Drop the oldest window block (index remap, no bytes move).  Sinks are never
+ * evicted.  SW_ERR_STATE if the window is empty or a NOISY append is due. */
+sw_status sw_cache_evict(sw_cache* c);
+
+/* Select the RoPE relocation policy and recompute the per-slot time bases
+ * (also recomputed after every commit and evict).  O(S+W+1) host work. */
+sw_status sw_rope_relocate(sw_cache* c, sw_rope_policy policy);
+
+/* Number of kept key tiles per query-tile row for keep fraction `keep_frac`
+ * in the current state: max(#forced, floor(keep_frac * n_key_tiles + 0.5)),
+ * n_key_tiles = (#logical slots) * ceil(B/128). */
+sw_status sw_tile_mask_budget(const sw_cache* c, float keep_frac, int32_t* k_row);
+
+/* Build the block-sparse tile mask from the raw queries q_raw [B][H][d] of this
+ * step: per head and 128-query tile, score every key tile by the dot product of
+ * mean relocated rotated query and key vectors / sqrt(d), keep key tile 0 of
+ * the first sink (if any) and the diagonal current tile, fill up to the budget
+ * with the highest scores (ties -> lower index).  Writes ascending linear key
+ * tile indices (slot * ceil(B/128) + tile) to tile_idx_out
+ * [H][ceil(B/128)][k_cap] (device int32); *k_row_out (host) = budget.
+ * Needs a sparse bf16 cache with a staged current block. */
+sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, float keep_frac,
+                             int32_t* tile_idx_out, int32_t k_cap, int32_t* k_row_out);
+
+/* One denoising step's chunk attention for the staged current block:
+ *   out[n][h] = softmax_k(<R(p_n) q_n, R(p_k) k> / sqrt(d)) V
+ * over keys [sinks, window oldest->newest, current], positions relocated by
+ * the current policy.  q_raw [B][H][d] raw (un-rotated) queries; out [B][H][d]
+ * in the cache dtype; lse_out (nullable) [H][B] fp32 natural-log sum of
+ * exp(score) per query.  tile_idx == NULL: dense; otherwise block-sparse over
+ * the key tiles listed in tile_idx [H][ceil(B/128)][k_row] (as written by
+ * sw_build_tile_mask; indices must be valid, may be unsorted but are then
+ * visited in the given order).  step selects the TwinCache copy. */
+sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step,
+                          const int32_t* tile_idx, int32_t k_row, void* out, float* lse_out);
+
+/* Logical slots in attention order (sinks, window oldest->newest, staged
+ * current).  Writes min(cap, count) entries; *n = count. Host-only. */
+sw_status sw_cache_inspect(const sw_cache* c, sw_slot_info* out, int32_t cap, int32_t* n);
+
+/* Copy logical slot `logical_slot`'s stored K (rotated at block-local
+ * positions) and V back out as token-major [B][H][d] device arrays (cache
+ * dtype).  kind: SW_KV_CLEAN or SW_KV_NOISY (history) / SW_KV_CURRENT (the
+ * staged block).  For tests and debugging; blocks until copied. */
+sw_status sw_cache_read_slot(sw_cache* c, int32_t logical_slot, sw_kv_kind kind, void* k_out,
+                             void* v_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWATTN_H */

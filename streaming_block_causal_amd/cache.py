@@ -1,0 +1,143 @@
+"""torch-facing wrapper of the C ABI: owns the device pool, checks tensors, calls native.
+
+Marshalling only -- device memory and streams come from PyTorch, all compute runs
+in libswattn's HIP kernels.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import native
+
+_DTYPES = {"bf16": (native.SW_BF16, torch.bfloat16), "f32": (native.SW_F32, torch.float32)}
+_POLICY = {"s1": native.SW_ROPE_S1_RELOCATE, "relative": native.SW_ROPE_RELATIVE_TIME}
+KIND = {"current": native.SW_KV_CURRENT, "clean": native.SW_KV_CLEAN, "noisy": native.SW_KV_NOISY}
+STEP = {"intermediate": native.SW_STEP_INTERMEDIATE, "final": native.SW_STEP_FINAL}
+
+
+@dataclasses.dataclass
+class CacheConfig:
+    n_heads: int
+    head_dim: int
+    frames_per_block: int
+    lat_h: int
+    lat_w: int
+    n_sink: int
+    n_window: int
+    twin: bool = False
+    sparse: bool = False
+    dtype: str = "bf16"
+    rope_theta: float = 10000.0
+    policy: str = "s1"
+    tile: int = 128
+
+    @property
+    def block_tokens(self) -> int:
+        return self.frames_per_block * self.lat_h * self.lat_w
+
+    def to_c(self) -> native.sw_cache_config:
+        return native.sw_cache_config(
+            n_heads=self.n_heads, head_dim=self.head_dim, frames_per_block=self.frames_per_block,
+            lat_h=self.lat_h, lat_w=self.lat_w, n_sink=self.n_sink, n_window=self.n_window,
+            twin=int(self.twin), sparse=int(self.sparse), dtype=_DTYPES[self.dtype][0],
+            rope_theta=self.rope_theta, policy=_POLICY[self.policy], tile=self.tile)
+
+
+class Cache:
+    """A sink + window KV cache on one GPU (or metadata-only with device=None)."""
+
+    def __init__(self, cfg: CacheConfig, device: Optional[str] = "cuda", stream: Optional[torch.cuda.Stream] = None):
+        self.cfg = cfg
+        self._c = cfg.to_c()
+        self.nbytes = native.sw_cache_required_bytes(self._c)
+        self.torch_dtype = _DTYPES[cfg.dtype][1]
+        self.shape = (cfg.block_tokens, cfg.n_heads, cfg.head_dim)
+        self.device = device
+        if device is None:
+            self.pool = None
+            self.stream = None
+            self.handle = native.sw_cache_create(self._c, 0, 0, 0)
+        else:
+            self.stream = stream if stream is not None else torch.cuda.current_stream(device)
+            self.pool = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+            self.handle = native.sw_cache_create(self._c, self.pool.data_ptr(), self.nbytes,
+                                                 self.stream.cuda_stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            native.sw_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- checks -----------------------------------------------------------------
+    def _tensor(self, t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+        if self.device is None:
+            return 1 if t is not None else 0          # metadata-only: only NULL-ness matters
+        dtype = dtype or self.torch_dtype
+        shape = shape or self.shape
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+        return t.data_ptr()
+
+    # ---- the C calls -----------------------------------------------------------
+    def append(self, kind: str, k: Optional[torch.Tensor], v: Optional[torch.Tensor], block_id: int):
+        kp = self._tensor(k, "k") if k is not None else 0
+        vp = self._tensor(v, "v") if v is not None else 0
+        native.sw_cache_append_block(self.handle, KIND[kind], kp, vp, block_id)
+
+    def evict(self):
+        native.sw_cache_evict(self.handle)
+
+    def relocate(self, policy: str):
+        native.sw_rope_relocate(self.handle, _POLICY[policy])
+
+    def mask_budget(self, keep_frac: float) -> int:
+        return native.sw_tile_mask_budget(self.handle, keep_frac)
+
+    def build_tile_mask(self, q: torch.Tensor, keep_frac: float, out: Optional[torch.Tensor] = None,
+                        k_cap: Optional[int] = None):
+        nt = -(-self.cfg.block_tokens // self.cfg.tile)
+        k_cap = k_cap or self.mask_budget(keep_frac)
+        if out is None:
+            out = torch.empty((self.cfg.n_heads, nt, k_cap), dtype=torch.int32, device=self.device)
+        op = self._tensor(out, "tile_idx_out", torch.int32, (self.cfg.n_heads, nt, k_cap))
+        k_row = native.sw_build_tile_mask(self.handle, self._tensor(q, "q"), keep_frac, op, k_cap)
+        return out, k_row
+
+    def attend(self, q: torch.Tensor, step: str = "final", tile_idx: Optional[torch.Tensor] = None,
+               k_row: int = 0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+        if out is None:
+            out = torch.empty(self.shape, dtype=self.torch_dtype, device=self.device)
+        tp = 0
+        if tile_idx is not None:
+            if tile_idx.dtype != torch.int32 or not tile_idx.is_cuda or not tile_idx.is_contiguous():
+                raise ValueError("tile_idx must be a contiguous int32 CUDA tensor")
+            nt = -(-self.cfg.block_tokens // self.cfg.tile)
+            if tuple(tile_idx.shape) != (self.cfg.n_heads, nt, k_row):
+                raise ValueError(f"tile_idx shape {tuple(tile_idx.shape)} != {(self.cfg.n_heads, nt, k_row)}")
+            tp = tile_idx.data_ptr()
+        lp = self._tensor(lse, "lse", torch.float32, (self.cfg.n_heads, self.cfg.block_tokens)) if lse is not None else 0
+        native.sw_chunk_attend(self.handle, self._tensor(q, "q"), STEP[step], tp, k_row,
+                               self._tensor(out, "out"), lp)
+        return out
+
+    def inspect(self):
+        return native.sw_cache_inspect(self.handle)
+
+    def read_slot(self, logical_slot: int, kind: str = "clean"):
+        k = torch.empty(self.shape, dtype=self.torch_dtype, device=self.device)
+        v = torch.empty_like(k)
+        native.sw_cache_read_slot(self.handle, logical_slot, KIND[kind], k.data_ptr(), v.data_ptr())
+        return k, v

@@ -1,0 +1,229 @@
+// K1: fused RoPE + KV append, and the cache read-back kernel.
+//
+// A block's raw K/V arrive token-major [B][H][d] (what a QKV projection writes).
+// The kernel rotates K at block-local positions (t = frame within the block, h,
+// w) -- the time relocation of each block is applied later to the queries, so a
+// stored block never has to be rewritten when the window slides (Vidu S2 vs
+// PixVerse R2 blog, section "Choice 3: bounded memory": RoPE relocation keeps
+// positions in the trained range) -- and stores K and V head-major so every
+// attention tile is one contiguous run of HBM.  bf16 V is stored transposed
+// (V^T [H][d][n_pad]) with keys permuted inside groups of 16 (perm16), the
+// operand order of the attention kernel's P.V MFMA.  Pad rows are zero.  For
+// block-sparse caches it also writes the fp32 mean of the rotated K of every
+// 128-token tile (valid tokens only), the pooled keys the tile mask scores.
+//
+// One workgroup per (128-token tile, head); HBM-bound: reads B*H*d raw K and V
+// once, writes them once.
+#include "device_common.h"
+
+namespace swattn {
+
+namespace {
+
+struct AppendArgs {
+  const void* k_raw;
+  const void* v_raw;
+  void* k_dst;
+  void* v_dst;
+  float* pooled;
+  int B, H, n_pad, nt, hw, lat_w;
+  RopeTab rt;
+};
+
+template <bool BF16>
+struct Elem;
+template <>
+struct Elem<true> {
+  typedef u16 T;
+  static __device__ __forceinline__ void load8(const u16* p, float* x) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store8(u16* p, const float* x) {
+    uint4 v;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(x[2 * i]) | ((uint32_t)f2bf(x[2 * i + 1]) << 16);
+    v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+    *reinterpret_cast<uint4*>(p) = v;
+  }
+};
+template <>
+struct Elem<false> {
+  typedef float T;
+  static __device__ __forceinline__ void load8(const float* p, float* x) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  static __device__ __forceinline__ void store8(float* p, const float* x) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+  }
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  typedef typename Elem<BF16>::T T;
+  constexpr int GPR = D / 8;              // 8-element groups per row
+  constexpr int ITEMS = kTile * GPR / 256;
+  constexpr int SUB = 256 / GPR;          // row sub-groups in the pooled reduction
+  __shared__ float red[SUB][D];
+  __shared__ __attribute__((aligned(16))) u16 vl[BF16 ? kTile : 1][D + 8];
+
+  const int tid = threadIdx.x, j = blockIdx.x, h = blockIdx.y;
+  const int grp = tid % GPR;
+  const T* kr = static_cast<const T*>(a.k_raw);
+  const T* vr = static_cast<const T*>(a.v_raw);
+  T* kd = static_cast<T*>(a.k_dst) + (size_t)h * a.n_pad * D;
+
+  float pacc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pacc[i] = 0.f;
+
+#pragma unroll 2
+  for (int it = 0; it < ITEMS; ++it) {
+    const int row = (tid + 256 * it) / GPR;
+    const int r = j * kTile + row;
+    float x[8];
+    if (r < a.B) {
+      Elem<BF16>::load8(kr + ((size_t)r * a.H + h) * D + grp * 8, x);
+      const int f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float c, s;
+        rope_cs(a.rt, grp * 4 + i, f, hh, ww, c, s);
+        const float x0 = x[2 * i], x1 = x[2 * i + 1];
+        x[2 * i] = x0 * c - x1 * s;
+        x[2 * i + 1] = x0 * s + x1 * c;
+        pacc[2 * i] += x[2 * i];
+        pacc[2 * i + 1] += x[2 * i + 1];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    }
+    Elem<BF16>::store8(kd + (size_t)r * D + grp * 8, x);
+
+    // V: raw row -> LDS (bf16, transposed below) or straight copy (fp32)
+    if (BF16) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < a.B) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(vr) +
+                                                       ((size_t)r * a.H + h) * D + grp * 8);
+      *reinterpret_cast<uint4*>(&vl[row][grp * 8]) = v;
+    } else {
+      float y[8];
+      if (r < a.B) {
+        Elem<BF16>::load8(vr + ((size_t)r * a.H + h) * D + grp * 8, y);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = 0.f;
+      }
+      T* vd = static_cast<T*>(a.v_dst) + ((size_t)h * a.n_pad + r) * D + grp * 8;
+      Elem<BF16>::store8(vd, y);
+    }
+  }
+
+  if (a.pooled) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[tid / GPR][grp * 8 + i] = pacc[i];
+  }
+  __syncthreads();
+
+  if (a.pooled && tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) s += red[i][tid];
+    const int cnt = min(kTile, a.B - j * kTile);
+    a.pooled[((size_t)h * a.nt + j) * D + tid] = s / (float)cnt;
+  }
+
+  if (BF16) {
+    // V^T rows: dd = feature, 16 chunks of 8 keys (perm16 order) per 128-key tile
+    u16* vt = static_cast<u16*>(a.v_dst) + (size_t)h * D * a.n_pad + (size_t)j * kTile;
+    constexpr int VITEMS = D * 16 / 256;
+#pragma unroll 2
+    for (int it = 0; it < VITEMS; ++it) {
+      const int c = tid + 256 * it;
+      const int dd = c >> 4, cc = c & 15;
+      const int g = cc >> 1, half = cc & 1;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k0 = 16 * g + perm16(8 * half + 2 * i);
+        const int k1 = 16 * g + perm16(8 * half + 2 * i + 1);
+        w[i] = (uint32_t)vl[k0][dd] | ((uint32_t)vl[k1][dd] << 16);
+      }
+      *reinterpret_cast<uint4*>(vt + (size_t)dd * a.n_pad + 8 * cc) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void unpack_kernel(const void* k_src, const void* v_src,
+                                                     void* k_out, void* v_out, int B, int H,
+                                                     int n_pad) {
+  typedef typename Elem<BF16>::T T;
+  const size_t total = (size_t)B * H * D;
+  for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * 256) {
+    const int dd = idx % D;
+    const int h = (idx / D) % H;
+    const int r = idx / ((size_t)H * D);
+    static_cast<T*>(k_out)[idx] = static_cast<const T*>(k_src)[((size_t)h * n_pad + r) * D + dd];
+    if (BF16) {
+      const int tile = r / kTile, in = r % kTile, g = in >> 4, c = perm16(in & 15);
+      static_cast<T*>(v_out)[idx] = static_cast<const T*>(
+          v_src)[((size_t)h * D + dd) * n_pad + (size_t)tile * kTile + 16 * g + c];
+    } else {
+      static_cast<T*>(v_out)[idx] = static_cast<const T*>(v_src)[((size_t)h * n_pad + r) * D + dd];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const Geometry& g, const RopeTab& rt, bool bf16, const void* k_raw,
+                         const void* v_raw, void* k_dst, void* v_dst, float* pooled_dst,
+                         hipStream_t stream) {
+  AppendArgs a{k_raw, v_raw, k_dst, v_dst, pooled_dst, g.B, g.H, g.n_pad, g.nt,
+               g.lat_h * g.lat_w, g.lat_w, rt};
+  const dim3 grid(g.nt, g.H), block(256);
+  if (bf16 && g.d == 128) {
+    hipLaunchKernelGGL((append_kernel<128, true>), grid, block, 0, stream, a);
+  } else if (!bf16 && g.d == 128) {
+    hipLaunchKernelGGL((append_kernel<128, false>), grid, block, 0, stream, a);
+  } else if (!bf16 && g.d == 64) {
+    hipLaunchKernelGGL((append_kernel<64, false>), grid, block, 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const Geometry& g, bool bf16, const void* k_src, const void* v_src,
+                         void* k_out, void* v_out, hipStream_t stream) {
+  const size_t total = (size_t)g.B * g.H * g.d;
+  const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+  if (bf16 && g.d == 128) {
+    hipLaunchKernelGGL((unpack_kernel<128, true>), dim3(blocks), dim3(256), 0, stream, k_src,
+                       v_src, k_out, v_out, g.B, g.H, g.n_pad);
+  } else if (!bf16 && g.d == 128) {
+    hipLaunchKernelGGL((unpack_kernel<128, false>), dim3(blocks), dim3(256), 0, stream, k_src,
+                       v_src, k_out, v_out, g.B, g.H, g.n_pad);
+  } else if (!bf16 && g.d == 64) {
+    hipLaunchKernelGGL((unpack_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, k_src,
+                       v_src, k_out, v_out, g.B, g.H, g.n_pad);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace swattn

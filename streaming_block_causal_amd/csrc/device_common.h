@@ -1,0 +1,55 @@
+// Device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace swattn {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ u16 f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(u16, h);
+}
+
+// cos/sin of RoPE pair p for a token at (t, h, w).
+__device__ __forceinline__ void rope_cs(const RopeTab& rt, int p, int t, int h, int w, float& c,
+                                        float& s) {
+  if (p < rt.pt) {
+    c = rt.cos_t[t * rt.pt + p];
+    s = rt.sin_t[t * rt.pt + p];
+  } else if (p < rt.pt + rt.ph) {
+    const int j = p - rt.pt;
+    c = rt.cos_h[h * rt.ph + j];
+    s = rt.sin_h[h * rt.ph + j];
+  } else {
+    const int j = p - rt.pt - rt.ph;
+    c = rt.cos_w[w * rt.pw + j];
+    s = rt.sin_w[w * rt.pw + j];
+  }
+}
+
+// Position of key c inside a 16-key group of the bf16 V^T cache layout.
+// Column c of a group holds key perm16(c): [0..3, 8..11, 4..7, 12..15]; the map is
+// its own inverse.  With it, the 8 keys one half-wave needs as the A operand of a
+// 32x32x16 MFMA (the rows of the 32x32 score tile it holds) are contiguous.
+__host__ __device__ __forceinline__ int perm16(int c) {
+  return (c >= 4 && c < 8) ? c + 4 : ((c >= 8 && c < 12) ? c - 4 : c);
+}
+
+// blockIdx -> task id so that consecutive tasks run on the same XCD (workgroups
+// are dealt to the 8 XCDs round-robin); keeps one head's K/V reads in one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int q = n >> 3, r = n & 7, x = bid & 7, loc = bid >> 3;
+  return (x < r) ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
+}
+
+}  // namespace swattn

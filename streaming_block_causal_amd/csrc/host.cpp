@@ -1,0 +1,538 @@
+// Host side of libswattn: the ring-buffer cache bookkeeping, RoPE tables,
+// argument validation and kernel dispatch behind the C ABI in include/swattn.h.
+//
+// Cache model ("Vidu S2 vs PixVerse R2" blog, section "Choice 3: bounded
+// memory"): the first S committed blocks are permanent sinks, later blocks go to
+// a window of the W most recent, older ones are evicted.  Physically there are
+// P = S + W + 1 slots (plus a noisy twin of each with TwinCache): the sinks, the
+// window and one staging slot the current block is written into every step.
+// Committing the staged block and evicting the oldest window block are pure
+// index remaps: the logical order lives in a small host table, a freed slot
+// becomes the next staging slot, and no K/V byte moves.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/swattn.h"
+#include "launch.h"
+
+using namespace swattn;
+
+namespace {
+
+thread_local std::string g_err;
+
+sw_status fail(sw_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sw_status fail(sw_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+sw_status hip_fail(hipError_t e, const char* what) {
+  return fail(SW_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace swhost {
+
+struct Entry {
+  int64_t block;
+  int phys;
+};
+
+struct Layout {
+  Geometry g;
+  size_t elem;           // bytes per stored element
+  size_t kv_bytes;       // one K (or V) buffer of a slot
+  size_t pooled_bytes;   // one pooled-key table of a slot (0 if not sparse)
+  int P;                 // physical slots
+  int t_len;             // time positions in the RoPE table
+  int pt, ph, pw;
+  size_t table_floats;
+  size_t total;
+};
+
+}  // namespace swhost
+
+using swhost::Entry;
+using swhost::Layout;
+
+namespace {
+
+sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
+  if (!cfg) return fail(SW_ERR_INVALID_ARG, "config is NULL");
+  const sw_cache_config& c = *cfg;
+  if (c.n_heads < 1 || c.frames_per_block < 1 || c.lat_h < 1 || c.lat_w < 1)
+    return fail(SW_ERR_INVALID_ARG, "n_heads, frames_per_block, lat_h, lat_w must be >= 1");
+  if (c.n_sink < 0 || c.n_window < 0) return fail(SW_ERR_INVALID_ARG, "n_sink, n_window must be >= 0");
+  if (c.n_sink + c.n_window + 1 > kMaxSlots)
+    return fail(SW_ERR_SHAPE, "n_sink + n_window + 1 = %d exceeds %d", c.n_sink + c.n_window + 1, kMaxSlots);
+  if (c.twin != 0 && c.twin != 1) return fail(SW_ERR_INVALID_ARG, "twin must be 0 or 1");
+  if (c.sparse != 0 && c.sparse != 1) return fail(SW_ERR_INVALID_ARG, "sparse must be 0 or 1");
+  if (c.dtype != SW_BF16 && c.dtype != SW_F32) return fail(SW_ERR_INVALID_ARG, "unknown dtype %d", (int)c.dtype);
+  if (c.policy != SW_ROPE_S1_RELOCATE && c.policy != SW_ROPE_RELATIVE_TIME)
+    return fail(SW_ERR_INVALID_ARG, "unknown RoPE policy %d", (int)c.policy);
+  if (!(c.rope_theta > 1.0) || !std::isfinite(c.rope_theta))
+    return fail(SW_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (c.tile != kTile) return fail(SW_ERR_UNSUPPORTED, "tile must be %d", kTile);
+  if (c.dtype == SW_BF16 && c.head_dim != 128)
+    return fail(SW_ERR_UNSUPPORTED, "bf16 kernels are built for head_dim 128 (got %d)", c.head_dim);
+  if (c.dtype == SW_F32 && c.head_dim != 64 && c.head_dim != 128)
+    return fail(SW_ERR_UNSUPPORTED, "fp32 kernels are built for head_dim 64 or 128 (got %d)", c.head_dim);
+  if (c.sparse && c.dtype != SW_BF16) return fail(SW_ERR_UNSUPPORTED, "block-sparse needs bf16");
+  const long long B = (long long)c.frames_per_block * c.lat_h * c.lat_w;
+  if (B > 65536) return fail(SW_ERR_SHAPE, "block of %lld tokens exceeds 65536", B);
+  Geometry& g = L->g;
+  g.B = (int)B;
+  g.H = c.n_heads;
+  g.d = c.head_dim;
+  g.F = c.frames_per_block;
+  g.lat_h = c.lat_h;
+  g.lat_w = c.lat_w;
+  g.nt = (g.B + kTile - 1) / kTile;
+  g.n_pad = g.nt * kTile;
+  if ((long long)(c.n_sink + c.n_window + 1) * g.nt > kMaxKeyTiles && c.sparse)
+    return fail(SW_ERR_SHAPE, "too many key tiles for the mask builder");
+  L->elem = c.dtype == SW_BF16 ? 2 : 4;
+  L->kv_bytes = align256((size_t)g.H * g.n_pad * g.d * L->elem);
+  L->pooled_bytes = c.sparse ? align256((size_t)g.H * g.nt * g.d * sizeof(float)) : 0;
+  L->P = c.n_sink + c.n_window + 1;
+  L->t_len = L->P * g.F;
+  const int pairs = g.d / 2;
+  L->ph = L->pw = pairs / 3;
+  L->pt = pairs - 2 * (pairs / 3);
+  L->table_floats = 2 * ((size_t)L->t_len * L->pt + (size_t)g.lat_h * L->ph + (size_t)g.lat_w * L->pw);
+  const int copies = c.twin ? 2 : 1;
+  L->total = (size_t)L->P * copies * (2 * L->kv_bytes + L->pooled_bytes) +
+             align256(L->table_floats * sizeof(float));
+  return SW_OK;
+}
+
+}  // namespace
+
+struct sw_cache {
+  sw_cache_config cfg;
+  Layout L;
+  bool dry;
+  hipStream_t stream;
+  char* pool;
+  RopeTab rt;
+  std::vector<char*> kc, vc, kn, vn;     // per physical slot: clean/current and noisy copies
+  std::vector<float*> pc, pn;            // pooled-key tables
+  std::vector<Entry> sinks;
+  std::deque<Entry> window;
+  std::deque<int> free_slots;
+  int staging;
+  bool staged;
+  int64_t staged_id;
+  bool have_commit;
+  int64_t last_commit;
+  bool noisy_due;
+  Entry noisy_entry;
+  sw_rope_policy policy;
+};
+
+namespace {
+
+// Time base of each logical slot [sinks, window oldest->newest, current].
+std::vector<int> bases_of(const sw_cache* c) {
+  const int ns = (int)c->sinks.size(), nw = (int)c->window.size(), F = c->L.g.F;
+  std::vector<int> b(ns + nw + 1);
+  for (int l = 0; l < ns + nw + 1; ++l) b[l] = l * F;
+  if (c->policy == SW_ROPE_RELATIVE_TIME)
+    for (int& x : b) x -= ns * F;
+  return b;
+}
+
+std::vector<Entry> history(const sw_cache* c) {
+  std::vector<Entry> h(c->sinks.begin(), c->sinks.end());
+  h.insert(h.end(), c->window.begin(), c->window.end());
+  return h;
+}
+
+void fill_tables(const Layout& L, double theta, std::vector<float>& t) {
+  t.assign(L.table_floats, 0.f);
+  size_t o = 0;
+  auto axis = [&](int n_pos, int n_pairs) {
+    for (int pos = 0; pos < n_pos; ++pos)
+      for (int j = 0; j < n_pairs; ++j) {
+        const double ang = (double)pos * std::pow(theta, -(double)j / (double)n_pairs);
+        t[o + (size_t)pos * n_pairs + j] = (float)std::cos(ang);
+        t[o + (size_t)n_pos * n_pairs + (size_t)pos * n_pairs + j] = (float)std::sin(ang);
+      }
+    o += 2 * (size_t)n_pos * n_pairs;
+  };
+  axis(L.t_len, L.pt);
+  axis(L.g.lat_h, L.ph);
+  axis(L.g.lat_w, L.pw);
+}
+
+sw_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(SW_ERR_INVALID_ARG, "%s is NULL", name);
+  return SW_OK;
+}
+
+sw_status write_block(sw_cache* c, const void* k, const void* v, char* kd, char* vd, float* pd) {
+  if (c->dry) return SW_OK;
+  const hipError_t e = launch_append(c->L.g, c->rt, c->cfg.dtype == SW_BF16, k, v, kd, vd, pd, c->stream);
+  if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+  return SW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sw_last_error(void) { return g_err.c_str(); }
+
+sw_status sw_cache_required_bytes(const sw_cache_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(SW_ERR_INVALID_ARG, "bytes is NULL");
+  Layout L;
+  const sw_status st = make_layout(cfg, &L);
+  if (st != SW_OK) return st;
+  *bytes = L.total;
+  return SW_OK;
+}
+
+sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t pool_bytes,
+                          void* hip_stream, sw_cache** out) {
+  if (!out) return fail(SW_ERR_INVALID_ARG, "out is NULL");
+  Layout L;
+  sw_status st = make_layout(cfg, &L);
+  if (st != SW_OK) return st;
+  const bool dry = device_pool == nullptr && pool_bytes == 0;
+  if (!dry) {
+    if (!device_pool) return fail(SW_ERR_INVALID_ARG, "device_pool is NULL");
+    if (((uintptr_t)device_pool & 255) != 0) return fail(SW_ERR_INVALID_ARG, "device_pool must be 256-byte aligned");
+    if (pool_bytes < L.total)
+      return fail(SW_ERR_CAPACITY, "pool of %zu bytes, %zu needed", pool_bytes, L.total);
+  }
+  sw_cache* c = new (std::nothrow) sw_cache();
+  if (!c) return fail(SW_ERR_CAPACITY, "host allocation failed");
+  c->cfg = *cfg;
+  c->L = L;
+  c->dry = dry;
+  c->stream = static_cast<hipStream_t>(hip_stream);
+  c->pool = static_cast<char*>(device_pool);
+  const int copies = cfg->twin ? 2 : 1;
+  c->kc.assign(L.P, nullptr);
+  c->vc.assign(L.P, nullptr);
+  c->kn.assign(L.P, nullptr);
+  c->vn.assign(L.P, nullptr);
+  c->pc.assign(L.P, nullptr);
+  c->pn.assign(L.P, nullptr);
+  if (!dry) {
+    char* p = c->pool;
+    for (int s = 0; s < L.P; ++s) {
+      for (int cp = 0; cp < copies; ++cp) {
+        char* kbuf = p; p += L.kv_bytes;
+        char* vbuf = p; p += L.kv_bytes;
+        float* pbuf = L.pooled_bytes ? reinterpret_cast<float*>(p) : nullptr;
+        p += L.pooled_bytes;
+        if (cp == 0) { c->kc[s] = kbuf; c->vc[s] = vbuf; c->pc[s] = pbuf; }
+        else { c->kn[s] = kbuf; c->vn[s] = vbuf; c->pn[s] = pbuf; }
+      }
+    }
+    float* tab = reinterpret_cast<float*>(p);
+    std::vector<float> host;
+    fill_tables(L, cfg->rope_theta, host);
+    hipError_t e = hipMemsetAsync(c->pool, 0, L.total, c->stream);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(tab, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) {
+      delete c;
+      return hip_fail(e, "cache initialisation");
+    }
+    size_t o = 0;
+    c->rt.cos_t = tab + o; o += (size_t)L.t_len * L.pt;
+    c->rt.sin_t = tab + o; o += (size_t)L.t_len * L.pt;
+    c->rt.cos_h = tab + o; o += (size_t)L.g.lat_h * L.ph;
+    c->rt.sin_h = tab + o; o += (size_t)L.g.lat_h * L.ph;
+    c->rt.cos_w = tab + o; o += (size_t)L.g.lat_w * L.pw;
+    c->rt.sin_w = tab + o;
+  }
+  c->rt.pt = L.pt;
+  c->rt.ph = L.ph;
+  c->rt.pw = L.pw;
+  c->rt.t_len = L.t_len;
+  c->staging = 0;
+  for (int s = 1; s < L.P; ++s) c->free_slots.push_back(s);
+  c->staged = false;
+  c->staged_id = -1;
+  c->have_commit = false;
+  c->last_commit = -1;
+  c->noisy_due = false;
+  c->noisy_entry = Entry{-1, -1};
+  c->policy = cfg->policy;
+  *out = c;
+  return SW_OK;
+}
+
+sw_status sw_cache_destroy(sw_cache* c) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  delete c;
+  return SW_OK;
+}
+
+sw_status sw_cache_append_block(sw_cache* c, sw_kv_kind kind, const void* k_raw, const void* v_raw,
+                                int64_t block_id) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  if (block_id < 0) return fail(SW_ERR_INVALID_ARG, "block_id must be >= 0");
+  const int S = c->cfg.n_sink, W = c->cfg.n_window;
+  switch (kind) {
+    case SW_KV_CURRENT: {
+      sw_status st = check_ptr(k_raw, "k_raw");
+      if (st == SW_OK) st = check_ptr(v_raw, "v_raw");
+      if (st != SW_OK) return st;
+      if (c->noisy_due) return fail(SW_ERR_STATE, "the noisy copy of block %lld must be appended first",
+                                    (long long)c->noisy_entry.block);
+      if (c->staged && block_id != c->staged_id)
+        return fail(SW_ERR_STATE, "block %lld is staged; commit it before staging block %lld",
+                    (long long)c->staged_id, (long long)block_id);
+      if (c->have_commit && block_id <= c->last_commit)
+        return fail(SW_ERR_STATE, "block %lld is not newer than the last commit %lld", (long long)block_id,
+                    (long long)c->last_commit);
+      const int s = c->staging;
+      st = write_block(c, k_raw, v_raw, c->kc[s], c->vc[s], c->pc[s]);
+      if (st != SW_OK) return st;
+      c->staged = true;
+      c->staged_id = block_id;
+      return SW_OK;
+    }
+    case SW_KV_CLEAN: {
+      if (c->noisy_due) return fail(SW_ERR_STATE, "the noisy copy of block %lld must be appended first",
+                                    (long long)c->noisy_entry.block);
+      const bool promote = k_raw == nullptr && v_raw == nullptr;
+      if (!promote) {
+        sw_status st = check_ptr(k_raw, "k_raw");
+        if (st == SW_OK) st = check_ptr(v_raw, "v_raw");
+        if (st != SW_OK) return st;
+        if (c->staged) return fail(SW_ERR_STATE, "a current block is staged; promote it with NULL pointers");
+      } else {
+        if (!c->staged) return fail(SW_ERR_STATE, "no staged current block to commit");
+        if (block_id != c->staged_id)
+          return fail(SW_ERR_STATE, "staged block is %lld, not %lld", (long long)c->staged_id, (long long)block_id);
+      }
+      if (c->have_commit && block_id <= c->last_commit)
+        return fail(SW_ERR_STATE, "block %lld is not newer than the last commit %lld", (long long)block_id,
+                    (long long)c->last_commit);
+      const bool to_sink = (int)c->sinks.size() < S;
+      if (!to_sink && W > 0 && (int)c->window.size() == W)
+        return fail(SW_ERR_CAPACITY, "window is full (%d blocks); evict first", W);
+      const bool dropped = !to_sink && W == 0;   // no window: the block leaves at once
+      int phys = -1;
+      if (!dropped) {
+        if (promote) {
+          if (c->free_slots.empty()) return fail(SW_ERR_STATE, "internal: no free slot for staging");
+          phys = c->staging;
+        } else {
+          if (c->free_slots.empty()) return fail(SW_ERR_STATE, "internal: no free slot");
+          phys = c->free_slots.front();
+          const sw_status st = write_block(c, k_raw, v_raw, c->kc[phys], c->vc[phys], c->pc[phys]);
+          if (st != SW_OK) return st;
+          c->free_slots.pop_front();
+        }
+      }
+      if (promote) {
+        c->staged = false;
+        c->staged_id = -1;
+        if (!dropped) {
+          c->staging = c->free_slots.front();
+          c->free_slots.pop_front();
+        }
+      }
+      c->have_commit = true;
+      c->last_commit = block_id;
+      if (!dropped) {
+        const Entry e{block_id, phys};
+        if (to_sink) c->sinks.push_back(e);
+        else c->window.push_back(e);
+        if (c->cfg.twin) {
+          c->noisy_due = true;
+          c->noisy_entry = e;
+        }
+      }
+      return SW_OK;
+    }
+    case SW_KV_NOISY: {
+      if (!c->cfg.twin) return fail(SW_ERR_STATE, "noisy copies need a TwinCache (twin = 1)");
+      sw_status st = check_ptr(k_raw, "k_raw");
+      if (st == SW_OK) st = check_ptr(v_raw, "v_raw");
+      if (st != SW_OK) return st;
+      if (!c->noisy_due) return fail(SW_ERR_STATE, "no committed block is waiting for its noisy copy");
+      if (block_id != c->noisy_entry.block)
+        return fail(SW_ERR_STATE, "noisy copy of block %lld is due, got %lld", (long long)c->noisy_entry.block,
+                    (long long)block_id);
+      const int s = c->noisy_entry.phys;
+      st = write_block(c, k_raw, v_raw, c->kn[s], c->vn[s], c->pn[s]);
+      if (st != SW_OK) return st;
+      c->noisy_due = false;
+      return SW_OK;
+    }
+  }
+  return fail(SW_ERR_INVALID_ARG, "unknown kv kind %d", (int)kind);
+}
+
+sw_status sw_cache_evict(sw_cache* c) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  if (c->noisy_due) return fail(SW_ERR_STATE, "the noisy copy of block %lld must be appended first",
+                                (long long)c->noisy_entry.block);
+  if (c->window.empty()) return fail(SW_ERR_STATE, "window is empty");
+  c->free_slots.push_back(c->window.front().phys);
+  c->window.pop_front();
+  return SW_OK;
+}
+
+sw_status sw_rope_relocate(sw_cache* c, sw_rope_policy policy) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  if (policy != SW_ROPE_S1_RELOCATE && policy != SW_ROPE_RELATIVE_TIME)
+    return fail(SW_ERR_INVALID_ARG, "unknown RoPE policy %d", (int)policy);
+  c->policy = policy;
+  return SW_OK;
+}
+
+sw_status sw_tile_mask_budget(const sw_cache* c, float keep_frac, int32_t* k_row) {
+  if (!c || !k_row) return fail(SW_ERR_INVALID_ARG, "cache or k_row is NULL");
+  if (!(keep_frac >= 0.f && keep_frac <= 1.f)) return fail(SW_ERR_INVALID_ARG, "keep_frac must be in [0, 1]");
+  const int n_slots = (int)(c->sinks.size() + c->window.size()) + 1;
+  const int n_kv = n_slots * c->L.g.nt;
+  const int n_forced = 1 + (c->sinks.empty() ? 0 : 1);
+  const int want = (int)std::floor((double)keep_frac * n_kv + 0.5);
+  *k_row = std::max(n_forced, std::min(want, n_kv));
+  return SW_OK;
+}
+
+sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, float keep_frac, int32_t* tile_idx_out,
+                             int32_t k_cap, int32_t* k_row_out) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  sw_status st = check_ptr(q_raw, "q_raw");
+  if (st == SW_OK) st = check_ptr(tile_idx_out, "tile_idx_out");
+  if (st == SW_OK) st = check_ptr(k_row_out, "k_row_out");
+  if (st != SW_OK) return st;
+  if (!c->cfg.sparse) return fail(SW_ERR_STATE, "cache was created without sparse = 1");
+  if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache cannot launch kernels");
+  if (!c->staged) return fail(SW_ERR_STATE, "no staged current block");
+  if (c->noisy_due) return fail(SW_ERR_STATE, "a noisy append is due");
+  int32_t k_row = 0;
+  st = sw_tile_mask_budget(c, keep_frac, &k_row);
+  if (st != SW_OK) return st;
+  if (k_row > k_cap) return fail(SW_ERR_CAPACITY, "k_cap %d < budget %d", k_cap, k_row);
+  const std::vector<Entry> hist = history(c);
+  const std::vector<int> b = bases_of(c);
+  const int n_slots = (int)hist.size() + 1;
+  const float* pooled[kMaxSlots];
+  int deltas[kMaxSlots];
+  for (int l = 0; l < n_slots; ++l) {
+    pooled[l] = l + 1 < n_slots ? c->pc[hist[l].phys] : c->pc[c->staging];
+    deltas[l] = b.back() - b[l];
+  }
+  const hipError_t e = launch_tile_mask(c->L.g, c->rt, q_raw, pooled, deltas, n_slots, !c->sinks.empty(),
+                                        k_row, k_cap, tile_idx_out, c->stream);
+  if (e != hipSuccess) return hip_fail(e, "tile mask kernel launch");
+  *k_row_out = k_row;
+  return SW_OK;
+}
+
+sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step, const int32_t* tile_idx,
+                          int32_t k_row, void* out, float* lse_out) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  sw_status st = check_ptr(q_raw, "q_raw");
+  if (st == SW_OK) st = check_ptr(out, "out");
+  if (st != SW_OK) return st;
+  if (step != SW_STEP_INTERMEDIATE && step != SW_STEP_FINAL)
+    return fail(SW_ERR_INVALID_ARG, "unknown step kind %d", (int)step);
+  if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache cannot launch kernels");
+  if (!c->staged) return fail(SW_ERR_STATE, "no staged current block (append SW_KV_CURRENT first)");
+  if (c->noisy_due) return fail(SW_ERR_STATE, "a noisy append is due");
+  if (tile_idx) {
+    if (c->cfg.dtype != SW_BF16) return fail(SW_ERR_UNSUPPORTED, "block-sparse attention needs bf16");
+    if (k_row < 1) return fail(SW_ERR_INVALID_ARG, "k_row must be >= 1 with a tile list");
+  }
+  const std::vector<Entry> hist = history(c);
+  const std::vector<int> b = bases_of(c);
+  const int n_slots = (int)hist.size() + 1;
+  if (tile_idx && k_row > n_slots * c->L.g.nt)
+    return fail(SW_ERR_INVALID_ARG, "k_row %d exceeds the %d key tiles", k_row, n_slots * c->L.g.nt);
+  const bool noisy = c->cfg.twin && step == SW_STEP_INTERMEDIATE;
+  SlotPtrs slots[kMaxSlots];
+  for (int l = 0; l + 1 < n_slots; ++l) {
+    const int p = hist[l].phys;
+    slots[l] = SlotPtrs{noisy ? c->kn[p] : c->kc[p], noisy ? c->vn[p] : c->vc[p], b.back() - b[l]};
+  }
+  slots[n_slots - 1] = SlotPtrs{c->kc[c->staging], c->vc[c->staging], 0};
+  const hipError_t e = launch_attend(c->L.g, c->rt, c->cfg.dtype == SW_BF16, q_raw, slots, n_slots, tile_idx,
+                                     k_row, out, lse_out, c->stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return SW_OK;
+}
+
+sw_status sw_cache_inspect(const sw_cache* c, sw_slot_info* out, int32_t cap, int32_t* n) {
+  if (!c || !n) return fail(SW_ERR_INVALID_ARG, "cache or n is NULL");
+  if (cap > 0 && !out) return fail(SW_ERR_INVALID_ARG, "out is NULL");
+  const std::vector<Entry> hist = history(c);
+  const std::vector<int> b = bases_of(c);
+  const int ns = (int)c->sinks.size();
+  const int count = (int)hist.size() + (c->staged ? 1 : 0);
+  for (int l = 0; l < count && l < cap; ++l) {
+    sw_slot_info& s = out[l];
+    if (l < (int)hist.size()) {
+      s.role = l < ns ? 0 : 1;
+      s.block_id = hist[l].block;
+      s.physical_slot = hist[l].phys;
+      s.twin_complete = (!c->cfg.twin || !(c->noisy_due && c->noisy_entry.phys == hist[l].phys)) ? 1 : 0;
+    } else {
+      s.role = 2;
+      s.block_id = c->staged_id;
+      s.physical_slot = c->staging;
+      s.twin_complete = 1;
+    }
+    s.time_base = b[l];
+  }
+  *n = count;
+  return SW_OK;
+}
+
+sw_status sw_cache_read_slot(sw_cache* c, int32_t logical_slot, sw_kv_kind kind, void* k_out, void* v_out) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  sw_status st = check_ptr(k_out, "k_out");
+  if (st == SW_OK) st = check_ptr(v_out, "v_out");
+  if (st != SW_OK) return st;
+  if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache holds no data");
+  const std::vector<Entry> hist = history(c);
+  int phys;
+  if (kind == SW_KV_CURRENT) {
+    if (!c->staged) return fail(SW_ERR_STATE, "no staged current block");
+    phys = c->staging;
+  } else {
+    if (logical_slot < 0 || logical_slot >= (int)hist.size())
+      return fail(SW_ERR_INVALID_ARG, "logical slot %d out of range [0, %d)", logical_slot, (int)hist.size());
+    if (kind == SW_KV_NOISY && !c->cfg.twin) return fail(SW_ERR_STATE, "no noisy copies without TwinCache");
+    if (kind != SW_KV_CLEAN && kind != SW_KV_NOISY) return fail(SW_ERR_INVALID_ARG, "unknown kv kind");
+    phys = hist[logical_slot].phys;
+  }
+  const bool noisy = kind == SW_KV_NOISY;
+  hipError_t e = launch_unpack(c->L.g, c->cfg.dtype == SW_BF16, noisy ? c->kn[phys] : c->kc[phys],
+                               noisy ? c->vn[phys] : c->vc[phys], k_out, v_out, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(e, "read-back");
+  return SW_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal interface between the host library (host.cpp) and the HIP kernels.
+// Not part of the public ABI (include/swattn.h is).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace swattn {
+
+constexpr int kMaxSlots = 16;     // S + W + 1
+constexpr int kTile = 128;        // block-sparse tile edge, query-tile rows
+constexpr int kMaxKeyTiles = 4096;
+
+// fp32 cos/sin tables (computed on the host in fp64) for the three RoPE axes.
+// time: [t_len][pt], height: [lat_h][ph], width: [lat_w][pw].
+struct RopeTab {
+  const float* cos_t; const float* sin_t;
+  const float* cos_h; const float* sin_h;
+  const float* cos_w; const float* sin_w;
+  int pt, ph, pw, t_len;
+};
+
+struct Geometry {
+  int B, H, d, F, lat_h, lat_w;
+  int n_pad;   // B rounded up to a multiple of 128
+  int nt;      // ceil(B / 128)
+};
+
+struct SlotPtrs {
+  const void* k;   // rotated K, [H][n_pad][d]
+  const void* v;   // bf16: V^T [H][d][n_pad] (keys permuted in groups of 16); fp32: V [H][n_pad][d]
+  int delta;       // time base of the current block minus this slot's
+};
+
+// K1: rotate K at block-local positions, store K and V head-major, pad rows zeroed,
+// optional per-tile fp32 means of rotated K ([H][nt][d]).
+hipError_t launch_append(const Geometry& g, const RopeTab& rt, bool bf16, const void* k_raw,
+                         const void* v_raw, void* k_dst, void* v_dst, float* pooled_dst,
+                         hipStream_t stream);
+
+// K2 / K3: chunk attention over the given slots (logical order); tile_idx == nullptr -> dense.
+hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const void* q,
+                         const SlotPtrs* slots, int n_slots, const int32_t* tile_idx, int k_row,
+                         void* out, float* lse, hipStream_t stream);
+
+// K4: block-sparse tile mask (bf16, d = 128).
+hipError_t launch_tile_mask(const Geometry& g, const RopeTab& rt, const void* q,
+                            const float* const* pooled, const int* deltas, int n_slots,
+                            bool has_sink, int k_row, int k_cap, int32_t* out, hipStream_t stream);
+
+// Read-back: cache layout -> token-major [B][H][d].
+hipError_t launch_unpack(const Geometry& g, bool bf16, const void* k_src, const void* v_src,
+                         void* k_out, void* v_out, hipStream_t stream);
+
+}  // namespace swattn

@@ -1,0 +1,164 @@
+// K4: block-sparse tile mask for one attention call (bf16, d = 128).
+//
+// R2 reaches >90% attention sparsity with block-sparse attention learned in
+// training (Vidu S2 vs PixVerse R2 blog, section "Choice 4: where the speed comes
+// from").  Without trained weights the mask is built from the data: per head and
+// 128-query tile, every 128-key tile of every cached block is scored by the dot
+// product of the mean relocated query and the mean relocated key / sqrt(d); key
+// tile 0 of the first sink (when there is a sink) and the diagonal current tile
+// are always kept, the remaining budget goes to the highest scores, ties to the
+// lower linear index.  Rotation is linear and the time rotation of a slot is the
+// same for all its tokens, so the relocated pooled query is the block-local
+// pooled query turned by R_t(delta_l) -- the pooled keys come from the append
+// kernel, rotated at block-local positions.
+//
+// One workgroup per (query tile, head).  Reads the query tile once (HBM-bound,
+// a few microseconds at 540p) and the tiny pooled-key tables.
+#include "device_common.h"
+
+namespace swattn {
+
+namespace {
+
+struct MaskArgs {
+  const u16* q;
+  int32_t* out;
+  int k_row, k_cap;
+  int B, H, nt, hw, lat_w;
+  int n_slots, has_sink;
+  float inv_sqrt_d;
+  RopeTab rt;
+  const float* pooled[kMaxSlots];
+  int delta[kMaxSlots];
+};
+
+__global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
+  constexpr int D = 128;
+  __shared__ float red[4][D];
+  __shared__ float qs[kMaxSlots][D];
+  __shared__ float sc[kMaxKeyTiles];
+  __shared__ unsigned char keep[kMaxKeyTiles];
+
+  const int tid = threadIdx.x, qt = blockIdx.x, h = blockIdx.y;
+  const int n_kv = a.n_slots * a.nt;
+
+  // 1. mean over the tile's valid queries of q rotated at block-local positions
+  {
+    const int p = tid & 63, rg = tid >> 6;
+    float s0 = 0.f, s1 = 0.f;
+    for (int i = 0; i < kTile / 4; ++i) {
+      const int r = qt * kTile + rg + 4 * i;
+      if (r >= a.B) break;
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(a.q + ((size_t)r * a.H + h) * D + 2 * p);
+      const int f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
+      float c, s;
+      rope_cs(a.rt, p, f, hh, ww, c, s);
+      const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
+      s0 += x0 * c - x1 * s;
+      s1 += x0 * s + x1 * c;
+    }
+    red[rg][2 * p] = s0;
+    red[rg][2 * p + 1] = s1;
+  }
+  __syncthreads();
+  // 2. relocate per slot: turn the time pairs by delta_l
+  if (tid < D / 2) {
+    const int p = tid;
+    const float cnt = (float)min(kTile, a.B - qt * kTile);
+    const float x0 = (red[0][2 * p] + red[1][2 * p] + red[2][2 * p] + red[3][2 * p]) / cnt;
+    const float x1 = (red[0][2 * p + 1] + red[1][2 * p + 1] + red[2][2 * p + 1] + red[3][2 * p + 1]) / cnt;
+    for (int sl = 0; sl < a.n_slots; ++sl) {
+      float c = 1.f, s = 0.f;
+      if (p < a.rt.pt) {
+        c = a.rt.cos_t[a.delta[sl] * a.rt.pt + p];
+        s = a.rt.sin_t[a.delta[sl] * a.rt.pt + p];
+      }
+      qs[sl][2 * p] = x0 * c - x1 * s;
+      qs[sl][2 * p + 1] = x0 * s + x1 * c;
+    }
+  }
+  __syncthreads();
+  // 3. scores of every key tile
+  for (int u = tid; u < n_kv; u += 256) {
+    const int sl = u / a.nt, jt = u - sl * a.nt;
+    const float4* kp = reinterpret_cast<const float4*>(a.pooled[sl] + ((size_t)h * a.nt + jt) * D);
+    float dot = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < D / 4; ++i) {
+      const float4 k4 = kp[i];
+      dot = fmaf(qs[sl][4 * i], k4.x, dot);
+      dot = fmaf(qs[sl][4 * i + 1], k4.y, dot);
+      dot = fmaf(qs[sl][4 * i + 2], k4.z, dot);
+      dot = fmaf(qs[sl][4 * i + 3], k4.w, dot);
+    }
+    sc[u] = dot * a.inv_sqrt_d;
+  }
+  __syncthreads();
+  // 4. forced tiles, then rank the rest: rank(u) = #better tiles (score, then lower index)
+  const int f_sink = a.has_sink ? 0 : -1;
+  const int f_diag = (a.n_slots - 1) * a.nt + qt;
+  const int n_forced = 1 + (f_sink >= 0 ? 1 : 0);
+  const int free_budget = a.k_row - n_forced;
+  for (int u = tid; u < n_kv; u += 256) {
+    bool k;
+    if (u == f_sink || u == f_diag) {
+      k = true;
+    } else {
+      const float su = sc[u];
+      int rank = 0;
+      for (int v = 0; v < n_kv; ++v) {
+        if (v == f_sink || v == f_diag || v == u) continue;
+        const float sv = sc[v];
+        rank += (sv > su || (sv == su && v < u)) ? 1 : 0;
+      }
+      k = rank < free_budget;
+    }
+    keep[u] = k ? 1 : 0;
+  }
+  __syncthreads();
+  // 5. ascending compaction by wave 0
+  if (tid < 64) {
+    int32_t* dst = a.out + ((size_t)h * a.nt + qt) * a.k_cap;
+    int count = 0;
+    for (int base = 0; base < n_kv; base += 64) {
+      const int u = base + tid;
+      const bool k = u < n_kv && keep[u];
+      const unsigned long long m = __ballot(k);
+      const int pos = count + __popcll(m & ((1ull << tid) - 1ull));
+      if (k && pos < a.k_cap) dst[pos] = u;
+      count += __popcll(m);
+    }
+    for (int pos = count + tid; pos < a.k_cap; pos += 64) dst[pos] = -1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tile_mask(const Geometry& g, const RopeTab& rt, const void* q,
+                            const float* const* pooled, const int* deltas, int n_slots,
+                            bool has_sink, int k_row, int k_cap, int32_t* out, hipStream_t stream) {
+  if (g.d != 128 || n_slots < 1 || n_slots > kMaxSlots || n_slots * g.nt > kMaxKeyTiles)
+    return hipErrorInvalidValue;
+  MaskArgs a;
+  a.q = static_cast<const u16*>(q);
+  a.out = out;
+  a.k_row = k_row;
+  a.k_cap = k_cap;
+  a.B = g.B;
+  a.H = g.H;
+  a.nt = g.nt;
+  a.hw = g.lat_h * g.lat_w;
+  a.lat_w = g.lat_w;
+  a.n_slots = n_slots;
+  a.has_sink = has_sink ? 1 : 0;
+  a.inv_sqrt_d = (float)(1.0 / __builtin_sqrt((double)g.d));
+  a.rt = rt;
+  for (int i = 0; i < kMaxSlots; ++i) {
+    a.pooled[i] = i < n_slots ? pooled[i] : nullptr;
+    a.delta[i] = i < n_slots ? deltas[i] : 0;
+  }
+  hipLaunchKernelGGL(tile_mask_kernel, dim3(g.nt, g.H), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace swattn
