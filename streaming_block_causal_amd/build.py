@@ -38,13 +38,14 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile and link; `defines` are extra -D flags (tuning variants), `out` the library path."""
+    os.makedirs(build_dir, exist_ok=True)
     objs, procs = [], []
     for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
@@ -59,10 +60,10 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             print(err, file=sys.stderr)
     if failed:
         raise RuntimeError("HIP build failed:\n" + "\n\n".join(failed))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
   const int tid = threadIdx.x, j = blockIdx.x, h = blockIdx.y;
   const int grp = tid % GPR;
+  const RopeTab rt = a.rt;
   const T* kr = static_cast<const T*>(a.k_raw);
   const T* vr = static_cast<const T*>(a.v_raw);
   T* kd = static_cast<T*>(a.k_dst) + (size_t)h * a.n_pad * D;
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float c, s;
-        rope_cs(a.rt, grp * 4 + i, f, hh, ww, c, s);
+        rope_cs(rt, grp * 4 + i, f, hh, ww, c, s);
         const float x0 = x[2 * i], x1 = x[2 * i + 1];
         x[2 * i] = x0 * c - x1 * s;
         x[2 * i + 1] = x0 * s + x1 * c;

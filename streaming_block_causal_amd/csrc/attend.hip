@@ -61,25 +61,86 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 // bf16 MFMA kernel
 // ------------------------------------------------------------------------------------
 constexpr int D = 128;
-constexpr int QW = 32;          // queries per wave
 constexpr int KB = 64;          // keys per LDS block
 constexpr int KS = D + 8;       // LDS row stride of K (bf16 elements)
 constexpr int VS = KB + 8;      // LDS row stride of V^T
+constexpr float kRescaleSlack = 8.0f;   // log2 units: exp2 arguments stay <= 8 between rescales
 
-template <bool SPARSE>
-__global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 ks[KB * KS];
-  __shared__ __attribute__((aligned(16))) u16 vs[D * VS];
+// Q^T operand of one wave: lane (hf, ln) holds q[row][16j + 8hf + 0..7] for j in [J0, J1), rotated
+// at time frame + delta (fp32 math, bf16 result).  Rows past the block give a zero operand.
+// Only the first kTimeJ operand groups hold time pairs (d = 128: 22 time pairs = dims 0..43), so a
+// new slot re-rotates those and the spatial groups are computed once per workgroup.
+constexpr int kTimeJ = 3;
+template <int J0, int J1>
+__device__ __forceinline__ void load_q(const RopeTab rt, const u16* qp, bool valid, int qf, int qh, int qw,
+                                       int hf, int delta, bf16x8 (&qb)[8]) {
+  const int t = qf + delta;
+#pragma unroll
+  for (int j = J0; j < J1; ++j) {
+    if (!valid) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qb[j][i] = (__bf16)0.f;
+      continue;
+    }
+    const uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * j + 8 * hf);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float c, s;
+      rope_cs(rt, 8 * j + 4 * hf + i, t, qh, qw, c, s);
+      const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xffff0000u);
+      qb[j][2 * i] = (__bf16)(x0 * c - x1 * s);
+      qb[j][2 * i + 1] = (__bf16)(x0 * s + x1 * c);
+    }
+  }
+}
+
+// Position i of a workgroup's key schedule -> (slot, 64-key block).  Dense: every block of every
+// slot in logical order.  Sparse: the two halves of each listed 128-key tile.  Returns false for
+// entries to skip (half of a short last tile, or an invalid tile index).
+__device__ __forceinline__ bool block_at(const int32_t* list, int n_slots, int nt, int nkb, int i, int& sl,
+                                         int& kb) {
+  if (list == nullptr) {
+    sl = i / nkb;
+    kb = i - sl * nkb;
+    return true;
+  }
+  const int tix = list[i >> 1];
+  if (tix < 0 || tix >= n_slots * nt) return false;   // never read outside the cache
+  sl = tix / nt;
+  kb = 2 * (tix - sl * nt) + (i & 1);
+  return kb < nkb;
+}
+
+// NW waves per workgroup, 32 queries per wave (the workgroup covers 32 * NW queries of one head).
+// The K/V blocks a workgroup streams are shared by all its waves through LDS.  Software pipeline:
+// the next block is fetched into registers while the current one is computed from LDS, then
+// stored into the other LDS buffer; one barrier per block.
+template <int NW, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void attend_bf16_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int LD = (KB * D / 8) / NT;   // 16-byte chunks per thread, K and V each
+  __shared__ __attribute__((aligned(16))) u16 ks[2][KB * KS];
+  __shared__ __attribute__((aligned(16))) u16 vs[2][D * VS];
+  __shared__ SlotPtrs sslot[kMaxSlots];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, ln = lane & 31;
+  // the argument struct is never addressed (that would copy it to scratch): static indices only
+#pragma unroll
+  for (int q = 0; q < kMaxSlots; ++q)
+    if (tid == q) sslot[q] = a.slot[q];
+  const RopeTab rt = a.rt;
+  __syncthreads();
+  const int n_qt = (a.B + 32 * NW - 1) / (32 * NW);
   const int task = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = task / a.nt, qt = task - h * a.nt;
-  const int qrow = qt * kTile + wave * QW + ln;
+  const int h = task / n_qt, qt = task - h * n_qt;
+  const int qrow = qt * 32 * NW + wave * 32 + ln;
   const bool qvalid = qrow < a.B;
-  const int qf = qrow / a.hw, qrem = qrow - qf * a.hw;
+  const int qf = qrow / a.hw;
+  const int qrem = qrow - qf * a.hw;
   const int qh = qrem / a.lat_w, qw = qrem - qh * a.lat_w;
-  const u16* qp = static_cast<const u16*>(a.q) + ((size_t)qrow * a.H + h) * D;
 
   f32x16 acc[4];
 #pragma unroll
@@ -89,129 +150,129 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   bf16x8 qb[8];
 
-  // Q^T operand for slot delta: lane (hf, ln) holds q[ln][16j + 8hf + 0..7], rotated.
-  auto load_q = [&](int delta) {
-    const int t = qf + delta;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (!qvalid) {   // rows past the block: zero operand, no table reads
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qb[j][i] = (__bf16)0.f;
-        continue;
-      }
-      const uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * j + 8 * hf);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float c, s;
-        rope_cs(a.rt, 8 * j + 4 * hf + i, t, qh, qw, c, s);
-        const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xffff0000u);
-        qb[j][2 * i] = (__bf16)(x0 * c - x1 * s);
-        qb[j][2 * i + 1] = (__bf16)(x0 * s + x1 * c);
-      }
-    }
-  };
+  const size_t kstride = (size_t)a.n_pad * D;   // per head, K and V^T alike
+  const int nkb = (a.B + KB - 1) / KB;
+  const int32_t* list = SPARSE ? a.tile_idx + ((size_t)h * a.nt + qt) * a.k_row : nullptr;
+  const int total = SPARSE ? 2 * a.k_row : a.n_slots * nkb;
 
-  auto do_block = [&](const u16* kbase, const u16* vbase, int kb) {
-    __syncthreads();   // previous block fully consumed
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 4, col = c & 15;
-      *reinterpret_cast<uint4*>(&ks[row * KS + col * 8]) =
-          *reinterpret_cast<const uint4*>(kbase + (size_t)(kb * KB + row) * D + col * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, dd = c >> 3, col = c & 7;
-      *reinterpret_cast<uint4*>(&vs[dd * VS + col * 8]) =
-          *reinterpret_cast<const uint4*>(vbase + (size_t)dd * a.n_pad + kb * KB + col * 8);
-    }
-    __syncthreads();
+  const u16* qp = static_cast<const u16*>(a.q) + ((size_t)qrow * a.H + h) * D;
+  load_q<kTimeJ, 8>(rt, qp, qvalid, qf, qh, qw, hf, 0, qb);
 
-    f32x16 s[2];
+  uint4 pk[LD], pv[LD];
+  int i = 0, sl = 0, kb = 0;
+  while (i < total && !block_at(list, a.n_slots, a.nt, nkb, i, sl, kb)) ++i;
+  if (i < total) {
+    const u16* kbase = static_cast<const u16*>(sslot[sl].k) + h * kstride;
+    const u16* vbase = static_cast<const u16*>(sslot[sl].v) + h * kstride;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int c0 = 0; c0 < LD; ++c0) {
+      const int c = tid + NT * c0;
+      pk[c0] = *reinterpret_cast<const uint4*>(kbase + (size_t)(kb * KB + (c >> 4)) * D + (c & 15) * 8);
+      pv[c0] = *reinterpret_cast<const uint4*>(vbase + (size_t)(c >> 3) * a.n_pad + kb * KB + (c & 7) * 8);
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+    for (int c0 = 0; c0 < LD; ++c0) {
+      const int c = tid + NT * c0;
+      *reinterpret_cast<uint4*>(&ks[0][(c >> 4) * KS + (c & 15) * 8]) = pk[c0];
+      *reinterpret_cast<uint4*>(&vs[0][(c >> 3) * VS + (c & 7) * 8]) = pv[c0];
+    }
+  }
+  __syncthreads();
+
+  int cur_slot = -1, buf = 0;
+  while (i < total) {
+    int j = i + 1, nsl = 0, nkb2 = 0;
+    while (j < total && !block_at(list, a.n_slots, a.nt, nkb, j, nsl, nkb2)) ++j;
+    const bool more = j < total;
+    if (more) {
+      const u16* kbase = static_cast<const u16*>(sslot[nsl].k) + h * kstride;
+      const u16* vbase = static_cast<const u16*>(sslot[nsl].v) + h * kstride;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&ks[(kt * 32 + ln) * KS + 16 * j + 8 * hf]);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qb[j], s[kt], 0, 0, 0);
+      for (int c0 = 0; c0 < LD; ++c0) {
+        const int c = tid + NT * c0;
+        pk[c0] = *reinterpret_cast<const uint4*>(kbase + (size_t)(nkb2 * KB + (c >> 4)) * D + (c & 15) * 8);
+        pv[c0] = *reinterpret_cast<const uint4*>(vbase + (size_t)(c >> 3) * a.n_pad + nkb2 * KB + (c & 7) * 8);
       }
+    }
+    if (sl != cur_slot) {
+      cur_slot = sl;
+      load_q<0, kTimeJ>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, qb);
+    }
+
+    // ---- S^T = K Q^T for 64 keys: two 32x32 tiles, lane holds 16 keys of query ln
+    const u16* kl = ks[buf];
+    const u16* vl = vs[buf];
+    f32x16 s0, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = 0.f;
+      s1[r] = 0.f;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(&kl[ln * KS + 16 * jj + 8 * hf]);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(&kl[(32 + ln) * KS + 16 * jj + 8 * hf]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qb[jj], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qb[jj], s1, 0, 0, 0);
     }
     const int kvalid = a.B - kb * KB;
     if (kvalid < KB) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= kvalid) s[kt][r] = -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key >= kvalid) s0[r] = -INFINITY;
+        if (key + 32 >= kvalid) s1[r] = -INFINITY;
+      }
     }
-    float mx = s[0][0];
+    // ---- online softmax (log2 domain, lazy rescale)
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    mx = swap_halves_max(mx) * a.scale_log2;
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = swap_halves_max(mx);
-    const float m_new = fmaxf(m_run, mx * a.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+    }
+    const float mneg = -m_run;
+    bf16x8 pb[4];
     float psum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], a.scale_log2, -m_new));
-        s[kt][r] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
-    bf16x8 pb[4];
+    for (int r = 0; r < 16; ++r) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], a.scale_log2, mneg));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], a.scale_log2, mneg));
+      psum += p0 + p1;
+      pb[r >> 3][r & 7] = (__bf16)p0;
+      pb[2 + (r >> 3)][r & 7] = (__bf16)p1;
+    }
+    l_run += psum;
+    // ---- O^T += V^T P^T
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[g][i] = (__bf16)s[g >> 1][8 * (g & 1) + i];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(&vs[(32 * t + ln) * VS + 16 * g + 8 * hf]);
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(&vl[(32 * t + ln) * VS + 16 * g + 8 * hf]);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[g], acc[t], 0, 0, 0);
       }
-  };
 
-  const int nkb = (a.B + KB - 1) / KB;
-  const size_t kstride = (size_t)a.n_pad * D;   // per head, K and V^T alike
-  if (!SPARSE) {
-    for (int sl = 0; sl < a.n_slots; ++sl) {
-      load_q(a.slot[sl].delta);
-      const u16* kbase = static_cast<const u16*>(a.slot[sl].k) + h * kstride;
-      const u16* vbase = static_cast<const u16*>(a.slot[sl].v) + h * kstride;
-      for (int kb = 0; kb < nkb; ++kb) do_block(kbase, vbase, kb);
-    }
-  } else {
-    const int32_t* list = a.tile_idx + ((size_t)h * a.nt + qt) * a.k_row;
-    int cur = -1;
-    const u16 *kbase = nullptr, *vbase = nullptr;
-    for (int i = 0; i < a.k_row; ++i) {
-      const int tix = list[i];
-      if (tix < 0 || tix >= a.n_slots * a.nt) continue;   // never read outside the cache
-      const int sl = tix / a.nt, jt = tix - sl * a.nt;
-      if (sl != cur) {
-        cur = sl;
-        load_q(a.slot[sl].delta);
-        kbase = static_cast<const u16*>(a.slot[sl].k) + h * kstride;
-        vbase = static_cast<const u16*>(a.slot[sl].v) + h * kstride;
+    if (more) {
+#pragma unroll
+      for (int c0 = 0; c0 < LD; ++c0) {
+        const int c = tid + NT * c0;
+        *reinterpret_cast<uint4*>(&ks[buf ^ 1][(c >> 4) * KS + (c & 15) * 8]) = pk[c0];
+        *reinterpret_cast<uint4*>(&vs[buf ^ 1][(c >> 3) * VS + (c & 7) * 8]) = pv[c0];
       }
-      do_block(kbase, vbase, 2 * jt);
-      if (2 * jt + 1 < nkb) do_block(kbase, vbase, 2 * jt + 1);
     }
+    __syncthreads();
+    buf ^= 1;
+    i = j;
+    sl = nsl;
+    kb = nkb2;
   }
 
   const float l_tot = swap_halves_sum(l_run);
@@ -240,7 +301,13 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
   constexpr int KBF = 32;
   __shared__ float kl[KBF][DD];
   __shared__ float vl[KBF][DD];
+  __shared__ SlotPtrs sslot[kMaxSlots];
   const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < kMaxSlots; ++q)
+    if (tid == q) sslot[q] = a.slot[q];
+  const RopeTab rt = a.rt;
+  __syncthreads();
   const int h = blockIdx.y;
   const int qrow = blockIdx.x * 64 + tid;
   const bool qvalid = qrow < a.B;
@@ -254,20 +321,20 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
   const float scale = a.scale_log2;
 
   for (int sl = 0; sl < a.n_slots; ++sl) {
-    const int t = qf + a.slot[sl].delta;
+    const int t = qf + sslot[sl].delta;
 #pragma unroll
     for (int p = 0; p < DD / 2; ++p) {
       float c = 1.f, s = 0.f, x0 = 0.f, x1 = 0.f;
       if (qvalid) {
-        rope_cs(a.rt, p, t, qh, qw, c, s);
+        rope_cs(rt, p, t, qh, qw, c, s);
         x0 = qp[2 * p];
         x1 = qp[2 * p + 1];
       }
       qr[2 * p] = x0 * c - x1 * s;
       qr[2 * p + 1] = x0 * s + x1 * c;
     }
-    const float* kbase = static_cast<const float*>(a.slot[sl].k) + (size_t)h * a.n_pad * DD;
-    const float* vbase = static_cast<const float*>(a.slot[sl].v) + (size_t)h * a.n_pad * DD;
+    const float* kbase = static_cast<const float*>(sslot[sl].k) + (size_t)h * a.n_pad * DD;
+    const float* vbase = static_cast<const float*>(sslot[sl].v) + (size_t)h * a.n_pad * DD;
     for (int k0 = 0; k0 < a.B; k0 += KBF) {
       __syncthreads();
       for (int i = tid; i < KBF * DD; i += 64) {
@@ -312,6 +379,11 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
+#ifndef SWATTN_DENSE_WAVES
+#define SWATTN_DENSE_WAVES 8
+#endif
+constexpr int kDenseWaves = SWATTN_DENSE_WAVES;
+
 hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const void* q,
                          const SlotPtrs* slots, int n_slots, const int32_t* tile_idx, int k_row,
                          void* out, float* lse, hipStream_t stream) {
@@ -334,11 +406,13 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
   for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0};
   if (bf16) {
     if (g.d != 128) return hipErrorInvalidValue;
-    const dim3 grid(g.nt * g.H), block(256);
-    if (tile_idx)
-      hipLaunchKernelGGL((attend_bf16_kernel<true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((attend_bf16_kernel<false>), grid, block, 0, stream, a);
+    if (tile_idx) {
+      hipLaunchKernelGGL((attend_bf16_kernel<4, true>), dim3(g.nt * g.H), dim3(256), 0, stream, a);
+    } else {
+      constexpr int NW = kDenseWaves;
+      const int n_qt = (g.B + 32 * NW - 1) / (32 * NW);
+      hipLaunchKernelGGL((attend_bf16_kernel<NW, false>), dim3(n_qt * g.H), dim3(64 * NW), 0, stream, a);
+    }
   } else {
     if (tile_idx) return hipErrorInvalidValue;
     const dim3 grid((g.B + 63) / 64, g.H), block(64);

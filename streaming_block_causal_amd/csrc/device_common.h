@@ -21,7 +21,7 @@ __device__ __forceinline__ u16 f2bf(float f) {
 }
 
 // cos/sin of RoPE pair p for a token at (t, h, w).
-__device__ __forceinline__ void rope_cs(const RopeTab& rt, int p, int t, int h, int w, float& c,
+__device__ __forceinline__ void rope_cs(const RopeTab rt, int p, int t, int h, int w, float& c,
                                         float& s) {
   if (p < rt.pt) {
     c = rt.cos_t[t * rt.pt + p];

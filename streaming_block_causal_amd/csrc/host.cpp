@@ -96,6 +96,9 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
   if (c.dtype == SW_F32 && c.head_dim != 64 && c.head_dim != 128)
     return fail(SW_ERR_UNSUPPORTED, "fp32 kernels are built for head_dim 64 or 128 (got %d)", c.head_dim);
   if (c.sparse && c.dtype != SW_BF16) return fail(SW_ERR_UNSUPPORTED, "block-sparse needs bf16");
+  // the bf16 attention kernel re-rotates only the first 24 pairs per slot: time pairs must fit
+  if (c.dtype == SW_BF16 && (c.head_dim / 2) - 2 * ((c.head_dim / 2) / 3) > 24)
+    return fail(SW_ERR_UNSUPPORTED, "time RoPE pairs exceed 24");
   const long long B = (long long)c.frames_per_block * c.lat_h * c.lat_w;
   if (B > 65536) return fail(SW_ERR_SHAPE, "block of %lld tokens exceeds 65536", B);
   Geometry& g = L->g;

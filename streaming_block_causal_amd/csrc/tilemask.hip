@@ -39,8 +39,18 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   __shared__ float sc[kMaxKeyTiles];
   __shared__ unsigned char keep[kMaxKeyTiles];
 
+  __shared__ const float* spooled[kMaxSlots];
+  __shared__ int sdelta[kMaxSlots];
   const int tid = threadIdx.x, qt = blockIdx.x, h = blockIdx.y;
   const int n_kv = a.n_slots * a.nt;
+  // the argument struct is never addressed (that would copy it to scratch): static indices only
+#pragma unroll
+  for (int q = 0; q < kMaxSlots; ++q)
+    if (tid == q) {
+      spooled[q] = a.pooled[q];
+      sdelta[q] = a.delta[q];
+    }
+  const RopeTab rt = a.rt;
 
   // 1. mean over the tile's valid queries of q rotated at block-local positions
   {
@@ -52,7 +62,7 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(a.q + ((size_t)r * a.H + h) * D + 2 * p);
       const int f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
       float c, s;
-      rope_cs(a.rt, p, f, hh, ww, c, s);
+      rope_cs(rt, p, f, hh, ww, c, s);
       const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
       s0 += x0 * c - x1 * s;
       s1 += x0 * s + x1 * c;
@@ -69,9 +79,9 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
     const float x1 = (red[0][2 * p + 1] + red[1][2 * p + 1] + red[2][2 * p + 1] + red[3][2 * p + 1]) / cnt;
     for (int sl = 0; sl < a.n_slots; ++sl) {
       float c = 1.f, s = 0.f;
-      if (p < a.rt.pt) {
-        c = a.rt.cos_t[a.delta[sl] * a.rt.pt + p];
-        s = a.rt.sin_t[a.delta[sl] * a.rt.pt + p];
+      if (p < rt.pt) {
+        c = rt.cos_t[sdelta[sl] * rt.pt + p];
+        s = rt.sin_t[sdelta[sl] * rt.pt + p];
       }
       qs[sl][2 * p] = x0 * c - x1 * s;
       qs[sl][2 * p + 1] = x0 * s + x1 * c;
@@ -81,7 +91,7 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   // 3. scores of every key tile
   for (int u = tid; u < n_kv; u += 256) {
     const int sl = u / a.nt, jt = u - sl * a.nt;
-    const float4* kp = reinterpret_cast<const float4*>(a.pooled[sl] + ((size_t)h * a.nt + jt) * D);
+    const float4* kp = reinterpret_cast<const float4*>(spooled[sl] + ((size_t)h * a.nt + jt) * D);
     float dot = 0.f;
 #pragma unroll 8
     for (int i = 0; i < D / 4; ++i) {
