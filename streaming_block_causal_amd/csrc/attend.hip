@@ -82,7 +82,7 @@ __device__ __forceinline__ void load_q(const RopeTab rt, const u16* qp, bool val
       for (int i = 0; i < 8; ++i) qb[j][i] = (__bf16)0.f;
       continue;
     }
-    const uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * j + 8 * hf);
+    const uint4 raw = ldg16(qp + 16 * j + 8 * hf);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -167,8 +167,8 @@ void attend_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int c0 = 0; c0 < LD; ++c0) {
       const int c = tid + NT * c0;
-      pk[c0] = *reinterpret_cast<const uint4*>(kbase + (size_t)(kb * KB + (c >> 4)) * D + (c & 15) * 8);
-      pv[c0] = *reinterpret_cast<const uint4*>(vbase + (size_t)(c >> 3) * a.n_pad + kb * KB + (c & 7) * 8);
+      pk[c0] = ldg16(kbase + (size_t)(kb * KB + (c >> 4)) * D + (c & 15) * 8);
+      pv[c0] = ldg16(vbase + (size_t)(c >> 3) * a.n_pad + kb * KB + (c & 7) * 8);
     }
 #pragma unroll
     for (int c0 = 0; c0 < LD; ++c0) {
@@ -190,8 +190,8 @@ void attend_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int c0 = 0; c0 < LD; ++c0) {
         const int c = tid + NT * c0;
-        pk[c0] = *reinterpret_cast<const uint4*>(kbase + (size_t)(nkb2 * KB + (c >> 4)) * D + (c & 15) * 8);
-        pv[c0] = *reinterpret_cast<const uint4*>(vbase + (size_t)(c >> 3) * a.n_pad + nkb2 * KB + (c & 7) * 8);
+        pk[c0] = ldg16(kbase + (size_t)(nkb2 * KB + (c >> 4)) * D + (c & 15) * 8);
+        pv[c0] = ldg16(vbase + (size_t)(c >> 3) * a.n_pad + nkb2 * KB + (c & 7) * 8);
       }
     }
     if (sl != cur_slot) {

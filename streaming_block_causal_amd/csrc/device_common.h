@@ -14,6 +14,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+// 16-byte load through the global address space.  Pointers fetched from LDS or
+// computed at run time are otherwise generic (flat) loads, which also count on the
+// LDS counter: waiting for an LDS operand would then wait for the HBM prefetch too.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  const u32x4 v = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(
+      reinterpret_cast<uintptr_t>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 __device__ __forceinline__ u16 f2bf(float f) {
   __bf16 h = (__bf16)f;
