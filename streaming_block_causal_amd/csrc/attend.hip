@@ -27,6 +27,8 @@
 //
 // fp32 path (d = 64 or 128): one thread per query, keys broadcast from LDS;
 // exact-ish reference-grade arithmetic for the small fp32 workload.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace swattn {
@@ -44,6 +46,10 @@ struct AttnArgs {
   int B, H, n_pad, nt, hw, lat_w;
   int n_slots;
   float scale_log2;   // log2(e) / sqrt(d)
+  int n_full;         // workgroups that own a whole query tile
+  int n_split;        // key-range pieces of each remaining tile (0: none)
+  float* part_o;      // [piece][128][128] normalised partial outputs of split tiles
+  float* part_lse;    // [piece][128] their log2 sum-exp
   RopeTab rt;
   SlotPtrs slot[kMaxSlots];
 };
@@ -112,14 +118,17 @@ __device__ __forceinline__ bool block_at(const int32_t* list, int n_slots, int n
   return kb < nkb;
 }
 
-// NW waves per workgroup, 32 queries per wave (the workgroup covers 32 * NW queries of one head).
-// The K/V blocks a workgroup streams are shared by all its waves through LDS.  Software pipeline:
-// the next block is fetched into registers while the current one is computed from LDS, then
-// stored into the other LDS buffer; one barrier per block.
-template <int NW, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+// One workgroup = 4 waves = 128 queries of one head (32 per wave); two workgroups share a CU.
+// The K/V blocks a workgroup streams are shared by its waves through LDS: the next block is
+// fetched into registers while the current one is computed, then stored into the other LDS
+// buffer; one barrier per block.
+// Workgroups past n_full each take 1/n_split of the key blocks of one of the remaining tiles
+// and write a normalised partial result; merge_kernel combines them.  This fills the last,
+// partial round of the grid instead of leaving most CUs idle.
+template <bool SPARSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_bf16_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
+  constexpr int NT = 256;
   constexpr int LD = (KB * D / 8) / NT;   // 16-byte chunks per thread, K and V each
   __shared__ __attribute__((aligned(16))) u16 ks[2][KB * KS];
   __shared__ __attribute__((aligned(16))) u16 vs[2][D * VS];
@@ -133,10 +142,21 @@ void attend_bf16_kernel(AttnArgs a) {
     if (tid == q) sslot[q] = a.slot[q];
   const RopeTab rt = a.rt;
   __syncthreads();
-  const int n_qt = (a.B + 32 * NW - 1) / (32 * NW);
-  const int task = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = task / n_qt, qt = task - h * n_qt;
-  const int qrow = qt * 32 * NW + wave * 32 + ln;
+
+  const int nkb = (a.B + KB - 1) / KB;
+  const int total = SPARSE ? 2 * a.k_row : a.n_slots * nkb;
+  int tile, i0 = 0, i1 = total, piece = -1;
+  if ((int)blockIdx.x < a.n_full) {
+    tile = xcd_remap(blockIdx.x, a.n_full);
+  } else {
+    piece = xcd_remap(blockIdx.x - a.n_full, gridDim.x - a.n_full);
+    const int part = piece % a.n_split;
+    tile = a.n_full + piece / a.n_split;
+    i0 = part * total / a.n_split;
+    i1 = (part + 1) * total / a.n_split;
+  }
+  const int h = tile / a.nt, qt = tile - h * a.nt;
+  const int qrow = qt * kTile + wave * 32 + ln;
   const bool qvalid = qrow < a.B;
   const int qf = qrow / a.hw;
   const int qrem = qrow - qf * a.hw;
@@ -151,17 +171,15 @@ void attend_bf16_kernel(AttnArgs a) {
   bf16x8 qb[8];
 
   const size_t kstride = (size_t)a.n_pad * D;   // per head, K and V^T alike
-  const int nkb = (a.B + KB - 1) / KB;
   const int32_t* list = SPARSE ? a.tile_idx + ((size_t)h * a.nt + qt) * a.k_row : nullptr;
-  const int total = SPARSE ? 2 * a.k_row : a.n_slots * nkb;
 
   const u16* qp = static_cast<const u16*>(a.q) + ((size_t)qrow * a.H + h) * D;
   load_q<kTimeJ, 8>(rt, qp, qvalid, qf, qh, qw, hf, 0, qb);
 
   uint4 pk[LD], pv[LD];
-  int i = 0, sl = 0, kb = 0;
-  while (i < total && !block_at(list, a.n_slots, a.nt, nkb, i, sl, kb)) ++i;
-  if (i < total) {
+  int i = i0, sl = 0, kb = 0;
+  while (i < i1 && !block_at(list, a.n_slots, a.nt, nkb, i, sl, kb)) ++i;
+  if (i < i1) {
     const u16* kbase = static_cast<const u16*>(sslot[sl].k) + h * kstride;
     const u16* vbase = static_cast<const u16*>(sslot[sl].v) + h * kstride;
 #pragma unroll
@@ -180,10 +198,10 @@ void attend_bf16_kernel(AttnArgs a) {
   __syncthreads();
 
   int cur_slot = -1, buf = 0;
-  while (i < total) {
+  while (i < i1) {
     int j = i + 1, nsl = 0, nkb2 = 0;
-    while (j < total && !block_at(list, a.n_slots, a.nt, nkb, j, nsl, nkb2)) ++j;
-    const bool more = j < total;
+    while (j < i1 && !block_at(list, a.n_slots, a.nt, nkb, j, nsl, nkb2)) ++j;
+    const bool more = j < i1;
     if (more) {
       const u16* kbase = static_cast<const u16*>(sslot[nsl].k) + h * kstride;
       const u16* vbase = static_cast<const u16*>(sslot[nsl].v) + h * kstride;
@@ -276,8 +294,21 @@ void attend_bf16_kernel(AttnArgs a) {
   }
 
   const float l_tot = swap_halves_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // an empty key range contributes nothing
+  if (piece >= 0) {   // partial result of a split tile: fp32, normalised, plus log2 sum-exp
+    const int row = wave * 32 + ln;
+    float* po = a.part_o + ((size_t)piece * kTile + row) * D;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *reinterpret_cast<float4*>(po + 32 * t + 8 * rg + 4 * hf) =
+            make_float4(acc[t][4 * rg] * inv, acc[t][4 * rg + 1] * inv, acc[t][4 * rg + 2] * inv,
+                        acc[t][4 * rg + 3] * inv);
+    if (hf == 0) a.part_lse[(size_t)piece * kTile + row] = m_run + __log2f(l_tot);
+    return;
+  }
   if (qvalid) {
-    const float inv = 1.f / l_tot;
     u16* op = static_cast<u16*>(a.o) + ((size_t)qrow * a.H + h) * D;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -290,6 +321,46 @@ void attend_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<uint2*>(op + d0) = w;
       }
     if (a.lse && hf == 0) a.lse[(size_t)h * a.B + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// Combine the n_split partial results of each split tile: weights 2^(lse_p - lse), lse the
+// log2 sum of 2^lse_p over the pieces (the softmax normaliser of the whole key range).
+constexpr int kMaxSplit = 32;
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
+  __shared__ float w[kMaxSplit][kTile];
+  const int tid = threadIdx.x, S = a.n_split;
+  const int tile = a.n_full + blockIdx.x;
+  const int h = tile / a.nt, qt = tile - h * a.nt;
+  const size_t p0 = (size_t)blockIdx.x * S;
+  if (tid < kTile) {
+    float mx = -INFINITY;
+    for (int p = 0; p < S; ++p) mx = fmaxf(mx, a.part_lse[(p0 + p) * kTile + tid]);
+    float sum = 0.f;
+    for (int p = 0; p < S; ++p) sum += __builtin_amdgcn_exp2f(a.part_lse[(p0 + p) * kTile + tid] - mx);
+    const float lse = mx + __log2f(sum);
+    for (int p = 0; p < S; ++p) w[p][tid] = __builtin_amdgcn_exp2f(a.part_lse[(p0 + p) * kTile + tid] - lse);
+    const int qrow = qt * kTile + tid;
+    if (a.lse && qrow < a.B) a.lse[(size_t)h * a.B + qrow] = lse * kLn2;
+  }
+  __syncthreads();
+  for (int e = tid; e < kTile * D / 4; e += 256) {
+    const int row = e / (D / 4), d4 = (e % (D / 4)) * 4;
+    const int qrow = qt * kTile + row;
+    if (qrow >= a.B) continue;
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int p = 0; p < S; ++p) {
+      const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((p0 + p) * kTile + row) * D + d4);
+      const float wp = w[p][row];
+      o0 = fmaf(wp, v.x, o0);
+      o1 = fmaf(wp, v.y, o1);
+      o2 = fmaf(wp, v.z, o2);
+      o3 = fmaf(wp, v.w, o3);
+    }
+    uint2 packed;
+    packed.x = (uint32_t)f2bf(o0) | ((uint32_t)f2bf(o1) << 16);
+    packed.y = (uint32_t)f2bf(o2) | ((uint32_t)f2bf(o3) << 16);
+    *reinterpret_cast<uint2*>(static_cast<u16*>(a.o) + ((size_t)qrow * a.H + h) * D + d4) = packed;
   }
 }
 
@@ -379,14 +450,9 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-#ifndef SWATTN_DENSE_WAVES
-#define SWATTN_DENSE_WAVES 8
-#endif
-constexpr int kDenseWaves = SWATTN_DENSE_WAVES;
-
 hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const void* q,
                          const SlotPtrs* slots, int n_slots, const int32_t* tile_idx, int k_row,
-                         void* out, float* lse, hipStream_t stream) {
+                         void* out, float* lse, const SplitPlan& plan, hipStream_t stream) {
   if (n_slots < 1 || n_slots > kMaxSlots) return hipErrorInvalidValue;
   AttnArgs a;
   a.q = q;
@@ -403,16 +469,32 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
   a.n_slots = n_slots;
   a.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)g.d));
   a.rt = rt;
+  a.part_o = plan.part_o;
+  a.part_lse = plan.part_lse;
   for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0};
+  const int tiles = g.nt * g.H;
   if (bf16) {
     if (g.d != 128) return hipErrorInvalidValue;
     if (tile_idx) {
-      hipLaunchKernelGGL((attend_bf16_kernel<4, true>), dim3(g.nt * g.H), dim3(256), 0, stream, a);
-    } else {
-      constexpr int NW = kDenseWaves;
-      const int n_qt = (g.B + 32 * NW - 1) / (32 * NW);
-      hipLaunchKernelGGL((attend_bf16_kernel<NW, false>), dim3(n_qt * g.H), dim3(64 * NW), 0, stream, a);
+      a.n_full = tiles;
+      a.n_split = 0;
+      hipLaunchKernelGGL((attend_bf16_kernel<true>), dim3(tiles), dim3(256), 0, stream, a);
+      return hipGetLastError();
     }
+    // tail split: whole rounds of `slots` workgroups own whole tiles; the tiles of a last,
+    // partial round are cut into up to kMaxSplit key ranges (only when a whole round exists)
+    const int conc = plan.concurrent;
+    const int tail = conc > 0 ? tiles % conc : 0;
+    int split = 0;
+    if (plan.part_o && conc > 0 && tiles >= conc && tail > 0) {
+      split = std::min(std::min(kMaxSplit, conc / tail), plan.max_pieces / tail);
+      split = std::min(split, n_slots * ((g.B + KB - 1) / KB));   // no empty key ranges
+      if (split < 2) split = 0;
+    }
+    a.n_full = split ? tiles - tail : tiles;
+    a.n_split = split;
+    hipLaunchKernelGGL((attend_bf16_kernel<false>), dim3(a.n_full + tail * split), dim3(256), 0, stream, a);
+    if (split) hipLaunchKernelGGL(merge_kernel, dim3(tail), dim3(256), 0, stream, a);
   } else {
     if (tile_idx) return hipErrorInvalidValue;
     const dim3 grid((g.B + 63) / 64, g.H), block(64);

@@ -65,6 +65,7 @@ struct Layout {
   int t_len;             // time positions in the RoPE table
   int pt, ph, pw;
   size_t table_floats;
+  size_t ws_bytes;       // partial results of split attention tiles (bf16 caches)
   size_t total;
 };
 
@@ -122,8 +123,12 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
   L->pt = pairs - 2 * (pairs / 3);
   L->table_floats = 2 * ((size_t)L->t_len * L->pt + (size_t)g.lat_h * L->ph + (size_t)g.lat_w * L->pw);
   const int copies = c.twin ? 2 : 1;
+  L->ws_bytes = c.dtype == SW_BF16
+                    ? align256((size_t)kMaxPieces * kTile * g.d * sizeof(float)) +
+                          align256((size_t)kMaxPieces * kTile * sizeof(float))
+                    : 0;
   L->total = (size_t)L->P * copies * (2 * L->kv_bytes + L->pooled_bytes) +
-             align256(L->table_floats * sizeof(float));
+             align256(L->table_floats * sizeof(float)) + L->ws_bytes;
   return SW_OK;
 }
 
@@ -149,6 +154,7 @@ struct sw_cache {
   bool noisy_due;
   Entry noisy_entry;
   sw_rope_policy policy;
+  SplitPlan plan;
 };
 
 namespace {
@@ -253,6 +259,19 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
       }
     }
     float* tab = reinterpret_cast<float*>(p);
+    p += align256(L.table_floats * sizeof(float));
+    c->plan.part_o = L.ws_bytes ? reinterpret_cast<float*>(p) : nullptr;
+    c->plan.part_lse = L.ws_bytes ? reinterpret_cast<float*>(p + align256((size_t)kMaxPieces * kTile * L.g.d * sizeof(float)))
+                                  : nullptr;
+    c->plan.max_pieces = L.ws_bytes ? kMaxPieces : 0;
+    int dev = 0, cus = 0;
+    hipError_t de = hipGetDevice(&dev);
+    if (de == hipSuccess) de = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (de != hipSuccess) {
+      delete c;
+      return hip_fail(de, "device query");
+    }
+    c->plan.concurrent = 2 * cus;   // the dense attention kernel runs two workgroups per CU
     std::vector<float> host;
     fill_tables(L, cfg->rope_theta, host);
     hipError_t e = hipMemsetAsync(c->pool, 0, L.total, c->stream);
@@ -284,6 +303,7 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
   c->noisy_due = false;
   c->noisy_entry = Entry{-1, -1};
   c->policy = cfg->policy;
+  if (dry) c->plan = SplitPlan{0, 0, nullptr, nullptr};
   *out = c;
   return SW_OK;
 }
@@ -481,7 +501,7 @@ sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step, con
   }
   slots[n_slots - 1] = SlotPtrs{c->kc[c->staging], c->vc[c->staging], 0};
   const hipError_t e = launch_attend(c->L.g, c->rt, c->cfg.dtype == SW_BF16, q_raw, slots, n_slots, tile_idx,
-                                     k_row, out, lse_out, c->stream);
+                                     k_row, out, lse_out, c->plan, c->stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return SW_OK;
 }

@@ -38,10 +38,20 @@ hipError_t launch_append(const Geometry& g, const RopeTab& rt, bool bf16, const 
                          const void* v_raw, void* k_dst, void* v_dst, float* pooled_dst,
                          hipStream_t stream);
 
+// Work split of the dense bf16 attention grid: `concurrent` = workgroups resident at once
+// (2 per CU); the workspace holds up to max_pieces partial 128-query results.
+struct SplitPlan {
+  int concurrent;
+  int max_pieces;
+  float* part_o;     // [max_pieces][128][128]
+  float* part_lse;   // [max_pieces][128]
+};
+constexpr int kMaxPieces = 512;
+
 // K2 / K3: chunk attention over the given slots (logical order); tile_idx == nullptr -> dense.
 hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const void* q,
                          const SlotPtrs* slots, int n_slots, const int32_t* tile_idx, int k_row,
-                         void* out, float* lse, hipStream_t stream);
+                         void* out, float* lse, const SplitPlan& plan, hipStream_t stream);
 
 // K4: block-sparse tile mask (bf16, d = 128).
 hipError_t launch_tile_mask(const Geometry& g, const RopeTab& rt, const void* q,

@@ -28,11 +28,15 @@ def test_required_bytes_closed_form():
     w = synth.WORKLOADS[2]
     c = config_for(w).to_c()
     n = native.sw_cache_required_bytes(c)
-    slot = 24 * 6144 * 128 * 2
-    table = 2 * (15 * 22 + 34 * 21 + 60 * 21) * 4
-    assert n == 5 * 2 * slot + ((table + 255) // 256) * 256
+    slot = 24 * 6144 * 128 * 2                       # one K (or V) slot, head-major, padded to 6144
+    table = 2 * (15 * 22 + 34 * 21 + 60 * 21) * 4     # fp32 cos/sin for t, h, w
+    work = 512 * 128 * 128 * 4 + 512 * 128 * 4       # partial results of split attention tiles
+    assert n == 5 * 2 * slot + ((table + 255) // 256) * 256 + work
     tw = config_for(synth.WORKLOADS[3]).to_c()
-    assert native.sw_cache_required_bytes(tw) == 5 * 4 * slot + ((table + 255) // 256) * 256
+    assert native.sw_cache_required_bytes(tw) == 5 * 4 * slot + ((table + 255) // 256) * 256 + work
+    f32 = config_for(synth.WORKLOADS[1]).to_c()
+    f32_table = 2 * (12 * 12 + 8 * 10 + 8 * 10) * 4    # 4 slots x 3 frames of time positions
+    assert native.sw_cache_required_bytes(f32) == 4 * 2 * (4 * 256 * 64 * 4) + ((f32_table + 255) // 256) * 256
 
 
 class _Dry:
