@@ -46,6 +46,7 @@ struct AttnArgs {
   int B, H, n_pad, nt, hw, lat_w;
   int n_slots;
   float scale_log2;   // log2(e) / sqrt(d)
+  int n_qt;           // query tiles per head of this launch
   int n_full;         // workgroups that own a whole query tile
   int n_split;        // key-range pieces of each remaining tile (0: none)
   float* part_o;      // [piece][128][128] normalised partial outputs of split tiles
@@ -70,7 +71,10 @@ constexpr int D = 128;
 constexpr int KB = 64;          // keys per LDS block
 constexpr int KS = D + 8;       // LDS row stride of K (bf16 elements)
 constexpr int VS = KB + 8;      // LDS row stride of V^T
-constexpr float kRescaleSlack = 8.0f;   // log2 units: exp2 arguments stay <= 8 between rescales
+constexpr float kRescaleSlack = 8.0f;
+#ifndef QK_AHEAD
+#define QK_AHEAD 2
+#endif   // log2 units: exp2 arguments stay <= 8 between rescales
 
 // Q^T operand of one wave: lane (hf, ln) holds q[row][16j + 8hf + 0..7] for j in [J0, J1), rotated
 // at time frame + delta (fp32 math, bf16 result).  Rows past the block give a zero operand.
@@ -118,33 +122,64 @@ __device__ __forceinline__ bool block_at(const int32_t* list, int n_slots, int n
   return kb < nkb;
 }
 
-// One workgroup = 4 waves = 128 queries of one head (32 per wave); two workgroups share a CU.
-// The K/V blocks a workgroup streams are shared by its waves through LDS: the next block is
-// fetched into registers while the current one is computed, then stored into the other LDS
-// buffer; one barrier per block.
+// Direct global -> LDS staging of one 64-key block (gfx950 global_load_lds_dwordx4: each lane
+// moves 16 bytes into LDS at base + 16 * lane, no registers involved).  LDS rows are unpadded and
+// XOR-swizzled so the MFMA operand reads are bank-conflict free:
+//   K  [64 keys][128 dims]: row r at r * 256 B, 16-byte chunk c at slot c ^ (r & 15)
+//   V^T[128 dims][64 keys]: row d at d * 128 B, 16-byte chunk c at slot c ^ ((d >> 1) & 7)
+// A workgroup's 4 waves each issue 4 K and 4 V instructions (1 KB each) per block.
+__device__ __forceinline__ void stage_block(const u16* kbase, const u16* vbase, int n_pad, int wave, int lane,
+                                            u16* kdst, u16* vdst) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int C = 4 * i + wave;   // 1 KB chunk of the block
+    const int r = 4 * C + (lane >> 4), ck = (lane & 15) ^ (r & 15);
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const __attribute__((address_space(1))) void*>(
+            reinterpret_cast<uintptr_t>(kbase + (size_t)r * D + 8 * ck)),
+        reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(kdst + C * 512)), 16,
+        0, 0);
+    const int d = 8 * C + (lane >> 3), cv = (lane & 7) ^ ((d >> 1) & 7);
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const __attribute__((address_space(1))) void*>(
+            reinterpret_cast<uintptr_t>(vbase + (size_t)d * n_pad + 8 * cv)),
+        reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(vdst + C * 512)), 16,
+        0, 0);
+  }
+}
+
+// One workgroup = 4 waves = 128 queries of one head (32 per wave); two workgroups share a CU
+// (<= 256 registers per wave, 64 KB of LDS each).  The K/V blocks a workgroup streams are shared
+// by its waves through LDS: while block n is computed from one buffer, block n+1 is already
+// landing in the other; one barrier per block.
 // Workgroups past n_full each take 1/n_split of the key blocks of one of the remaining tiles
 // and write a normalised partial result; merge_kernel combines them.  This fills the last,
 // partial round of the grid instead of leaving most CUs idle.
-template <bool SPARSE>
+template <bool SPARSE, int NQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_bf16_kernel(AttnArgs a) {
-  constexpr int NT = 256;
-  constexpr int LD = (KB * D / 8) / NT;   // 16-byte chunks per thread, K and V each
-  __shared__ __attribute__((aligned(16))) u16 ks[2][KB * KS];
-  __shared__ __attribute__((aligned(16))) u16 vs[2][D * VS];
+  static_assert(NQ == 1, "one 32-query sub-tile per wave");
+  constexpr int ROWS = 128;
+  __shared__ __attribute__((aligned(1024))) u16 ks0[KB * D];
+  __shared__ __attribute__((aligned(1024))) u16 ks1[KB * D];
+  __shared__ __attribute__((aligned(1024))) u16 vs0[D * KB];
+  __shared__ __attribute__((aligned(1024))) u16 vs1[D * KB];
   __shared__ SlotPtrs sslot[kMaxSlots];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, ln = lane & 31;
-  // the argument struct is never addressed (that would copy it to scratch): static indices only
+  // the argument struct is never addressed (that would copy it to scratch): static indices only,
+  // and every field the lambdas below need is copied to a local first
 #pragma unroll
   for (int q = 0; q < kMaxSlots; ++q)
     if (tid == q) sslot[q] = a.slot[q];
   const RopeTab rt = a.rt;
+  const int B = a.B, n_pad = a.n_pad, n_slots = a.n_slots, nt = a.nt;
+  const float scale_log2 = a.scale_log2;
   __syncthreads();
 
-  const int nkb = (a.B + KB - 1) / KB;
-  const int total = SPARSE ? 2 * a.k_row : a.n_slots * nkb;
+  const int nkb = (B + KB - 1) / KB;
+  const int total = SPARSE ? 2 * a.k_row : n_slots * nkb;
   int tile, i0 = 0, i1 = total, piece = -1;
   if ((int)blockIdx.x < a.n_full) {
     tile = xcd_remap(blockIdx.x, a.n_full);
@@ -155,12 +190,13 @@ void attend_bf16_kernel(AttnArgs a) {
     i0 = part * total / a.n_split;
     i1 = (part + 1) * total / a.n_split;
   }
-  const int h = tile / a.nt, qt = tile - h * a.nt;
-  const int qrow = qt * kTile + wave * 32 + ln;
-  const bool qvalid = qrow < a.B;
+  const int h = tile / a.n_qt, qt = tile - h * a.n_qt;
+  const int qrow = qt * ROWS + wave * 32 + ln;
+  const bool qvalid = qrow < B;
   const int qf = qrow / a.hw;
   const int qrem = qrow - qf * a.hw;
   const int qh = qrem / a.lat_w, qw = qrem - qh * a.lat_w;
+  const u16* qp = static_cast<const u16*>(a.q) + ((size_t)qrow * a.H + h) * D;
 
   f32x16 acc[4];
 #pragma unroll
@@ -169,71 +205,57 @@ void attend_bf16_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   bf16x8 qb[8];
-
-  const size_t kstride = (size_t)a.n_pad * D;   // per head, K and V^T alike
-  const int32_t* list = SPARSE ? a.tile_idx + ((size_t)h * a.nt + qt) * a.k_row : nullptr;
-
-  const u16* qp = static_cast<const u16*>(a.q) + ((size_t)qrow * a.H + h) * D;
   load_q<kTimeJ, 8>(rt, qp, qvalid, qf, qh, qw, hf, 0, qb);
 
-  uint4 pk[LD], pv[LD];
-  int i = i0, sl = 0, kb = 0;
-  while (i < i1 && !block_at(list, a.n_slots, a.nt, nkb, i, sl, kb)) ++i;
-  if (i < i1) {
-    const u16* kbase = static_cast<const u16*>(sslot[sl].k) + h * kstride;
-    const u16* vbase = static_cast<const u16*>(sslot[sl].v) + h * kstride;
+  // per-lane byte offsets of the swizzled operand reads (see stage_block)
+  int koff[8], voff[4];
 #pragma unroll
-    for (int c0 = 0; c0 < LD; ++c0) {
-      const int c = tid + NT * c0;
-      pk[c0] = ldg16(kbase + (size_t)(kb * KB + (c >> 4)) * D + (c & 15) * 8);
-      pv[c0] = ldg16(vbase + (size_t)(c >> 3) * a.n_pad + kb * KB + (c & 7) * 8);
-    }
+  for (int jj = 0; jj < 8; ++jj) koff[jj] = ln * 128 + 8 * ((2 * jj + hf) ^ (ln & 15));
 #pragma unroll
-    for (int c0 = 0; c0 < LD; ++c0) {
-      const int c = tid + NT * c0;
-      *reinterpret_cast<uint4*>(&ks[0][(c >> 4) * KS + (c & 15) * 8]) = pk[c0];
-      *reinterpret_cast<uint4*>(&vs[0][(c >> 3) * VS + (c & 7) * 8]) = pv[c0];
-    }
-  }
-  __syncthreads();
+  for (int g = 0; g < 4; ++g) voff[g] = ln * 64 + 8 * ((2 * g + hf) ^ ((ln >> 1) & 7));
 
-  int cur_slot = -1, buf = 0;
-  while (i < i1) {
-    int j = i + 1, nsl = 0, nkb2 = 0;
-    while (j < i1 && !block_at(list, a.n_slots, a.nt, nkb, j, nsl, nkb2)) ++j;
-    const bool more = j < i1;
-    if (more) {
-      const u16* kbase = static_cast<const u16*>(sslot[nsl].k) + h * kstride;
-      const u16* vbase = static_cast<const u16*>(sslot[nsl].v) + h * kstride;
-#pragma unroll
-      for (int c0 = 0; c0 < LD; ++c0) {
-        const int c = tid + NT * c0;
-        pk[c0] = ldg16(kbase + (size_t)(nkb2 * KB + (c >> 4)) * D + (c & 15) * 8);
-        pv[c0] = ldg16(vbase + (size_t)(c >> 3) * a.n_pad + nkb2 * KB + (c & 7) * 8);
-      }
-    }
-    if (sl != cur_slot) {
-      cur_slot = sl;
-      load_q<0, kTimeJ>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, qb);
-    }
+  const size_t kstride = (size_t)n_pad * D;   // per head, K and V^T alike
+  const int32_t* list = SPARSE ? a.tile_idx + ((size_t)h * nt + qt) * a.k_row : nullptr;
 
+  auto stage = [&](int s, int kb, u16* kdst, u16* vdst) {
+    stage_block(static_cast<const u16*>(sslot[s].k) + h * kstride + (size_t)kb * KB * D,
+                static_cast<const u16*>(sslot[s].v) + h * kstride + kb * KB, n_pad, wave, lane, kdst, vdst);
+  };
+
+  auto compute = [&](const u16* kl, const u16* vl, int kb) {
     // ---- S^T = K Q^T for 64 keys: two 32x32 tiles, lane holds 16 keys of query ln
-    const u16* kl = ks[buf];
-    const u16* vl = vs[buf];
     f32x16 s0, s1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] = 0.f;
       s1[r] = 0.f;
     }
+    // operands are read QK_AHEAD steps ahead of their MFMAs; the schedule is pinned below
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 kop[QK_AHEAD + 1][2];
+#pragma unroll
+    for (int jj = 0; jj < QK_AHEAD; ++jj) {
+      kop[jj][0] = *reinterpret_cast<const bf16x8*>(kl + koff[jj]);
+      kop[jj][1] = *reinterpret_cast<const bf16x8*>(kl + 32 * D + koff[jj]);
+    }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(&kl[ln * KS + 16 * jj + 8 * hf]);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(&kl[(32 + ln) * KS + 16 * jj + 8 * hf]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qb[jj], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qb[jj], s1, 0, 0, 0);
+      if (jj + QK_AHEAD < 8) {
+        kop[(jj + QK_AHEAD) % (QK_AHEAD + 1)][0] = *reinterpret_cast<const bf16x8*>(kl + koff[jj + QK_AHEAD]);
+        kop[(jj + QK_AHEAD) % (QK_AHEAD + 1)][1] =
+            *reinterpret_cast<const bf16x8*>(kl + 32 * D + koff[jj + QK_AHEAD]);
+      }
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[jj % (QK_AHEAD + 1)][0], qb[jj], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[jj % (QK_AHEAD + 1)][1], qb[jj], s1, 0, 0, 0);
     }
-    const int kvalid = a.B - kb * KB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * QK_AHEAD, 0);   // the first reads
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (jj + QK_AHEAD < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                         // two MFMAs
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int kvalid = B - kb * KB;
     if (kvalid < KB) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -246,7 +268,7 @@ void attend_bf16_kernel(AttnArgs a) {
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = swap_halves_max(mx) * a.scale_log2;
+    mx = swap_halves_max(mx) * scale_log2;
     if (__any(mx > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -259,45 +281,64 @@ void attend_bf16_kernel(AttnArgs a) {
     }
     const float mneg = -m_run;
     bf16x8 pb[4];
-    float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], a.scale_log2, mneg));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], a.scale_log2, mneg));
-      psum += p0 + p1;
-      pb[r >> 3][r & 7] = (__bf16)p0;
-      pb[2 + (r >> 3)][r & 7] = (__bf16)p1;
+      pb[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, mneg));
+      pb[2 + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, mneg));
     }
-    l_run += psum;
+    // row sum of the bf16 probabilities that multiply V (packed pairs, v_dot2c_f32_bf16)
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pair = {pb[g][2 * e], pb[g][2 * e + 1]};
+        ps[g] = __builtin_amdgcn_fdot2_f32_bf16(pair, one2, ps[g], false);
+      }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(&vl[(32 * t + ln) * VS + 16 * g + 8 * hf]);
+        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vl + 32 * t * KB + voff[g]);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[g], acc[t], 0, 0, 0);
       }
+  };
 
-    if (more) {
-#pragma unroll
-      for (int c0 = 0; c0 < LD; ++c0) {
-        const int c = tid + NT * c0;
-        *reinterpret_cast<uint4*>(&ks[buf ^ 1][(c >> 4) * KS + (c & 15) * 8]) = pk[c0];
-        *reinterpret_cast<uint4*>(&vs[buf ^ 1][(c >> 3) * VS + (c & 7) * 8]) = pv[c0];
-      }
+  int i = i0, sl = 0, kb = 0;
+  while (i < i1 && !block_at(list, n_slots, nt, nkb, i, sl, kb)) ++i;
+  if (i < i1) stage(sl, kb, ks0, vs0);
+  int cur_slot = -1;
+
+  // one pipeline step: block (sl, kb) is in (kc, vc); the next one goes to (kn, vn)
+  auto step = [&](const u16* kc, const u16* vc, u16* kn, u16* vn) {
+    int j = i + 1, nsl = 0, nkb2 = 0;
+    while (j < i1 && !block_at(list, n_slots, nt, nkb, j, nsl, nkb2)) ++j;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of block i has landed
+    __syncthreads();                      // ... and everyone's; buffer (kn, vn) is free again
+    if (j < i1) stage(nsl, nkb2, kn, vn);
+    if (sl != cur_slot) {
+      cur_slot = sl;
+      load_q<0, kTimeJ>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, qb);
     }
-    __syncthreads();
-    buf ^= 1;
+    compute(kc, vc, kb);
     i = j;
     sl = nsl;
     kb = nkb2;
+  };
+  while (i < i1) {
+    step(ks0, vs0, ks1, vs1);
+    if (i >= i1) break;
+    step(ks1, vs1, ks0, vs0);
   }
 
   const float l_tot = swap_halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // an empty key range contributes nothing
   if (piece >= 0) {   // partial result of a split tile: fp32, normalised, plus log2 sum-exp
     const int row = wave * 32 + ln;
-    float* po = a.part_o + ((size_t)piece * kTile + row) * D;
+    float* po = a.part_o + ((size_t)piece * ROWS + row) * D;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -305,7 +346,7 @@ void attend_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<float4*>(po + 32 * t + 8 * rg + 4 * hf) =
             make_float4(acc[t][4 * rg] * inv, acc[t][4 * rg + 1] * inv, acc[t][4 * rg + 2] * inv,
                         acc[t][4 * rg + 3] * inv);
-    if (hf == 0) a.part_lse[(size_t)piece * kTile + row] = m_run + __log2f(l_tot);
+    if (hf == 0) a.part_lse[(size_t)piece * ROWS + row] = m_run + __log2f(l_tot);
     return;
   }
   if (qvalid) {
@@ -320,37 +361,38 @@ void attend_bf16_kernel(AttnArgs a) {
         w.y = (uint32_t)f2bf(acc[t][4 * rg + 2] * inv) | ((uint32_t)f2bf(acc[t][4 * rg + 3] * inv) << 16);
         *reinterpret_cast<uint2*>(op + d0) = w;
       }
-    if (a.lse && hf == 0) a.lse[(size_t)h * a.B + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    if (a.lse && hf == 0) a.lse[(size_t)h * B + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   }
 }
 
 // Combine the n_split partial results of each split tile: weights 2^(lse_p - lse), lse the
 // log2 sum of 2^lse_p over the pieces (the softmax normaliser of the whole key range).
 constexpr int kMaxSplit = 32;
+template <int ROWS>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
-  __shared__ float w[kMaxSplit][kTile];
+  __shared__ float w[kMaxSplit][ROWS];
   const int tid = threadIdx.x, S = a.n_split;
   const int tile = a.n_full + blockIdx.x;
-  const int h = tile / a.nt, qt = tile - h * a.nt;
+  const int h = tile / a.n_qt, qt = tile - h * a.n_qt;
   const size_t p0 = (size_t)blockIdx.x * S;
-  if (tid < kTile) {
+  for (int row = tid; row < ROWS; row += 256) {
     float mx = -INFINITY;
-    for (int p = 0; p < S; ++p) mx = fmaxf(mx, a.part_lse[(p0 + p) * kTile + tid]);
+    for (int p = 0; p < S; ++p) mx = fmaxf(mx, a.part_lse[(p0 + p) * ROWS + row]);
     float sum = 0.f;
-    for (int p = 0; p < S; ++p) sum += __builtin_amdgcn_exp2f(a.part_lse[(p0 + p) * kTile + tid] - mx);
+    for (int p = 0; p < S; ++p) sum += __builtin_amdgcn_exp2f(a.part_lse[(p0 + p) * ROWS + row] - mx);
     const float lse = mx + __log2f(sum);
-    for (int p = 0; p < S; ++p) w[p][tid] = __builtin_amdgcn_exp2f(a.part_lse[(p0 + p) * kTile + tid] - lse);
-    const int qrow = qt * kTile + tid;
+    for (int p = 0; p < S; ++p) w[p][row] = __builtin_amdgcn_exp2f(a.part_lse[(p0 + p) * ROWS + row] - lse);
+    const int qrow = qt * ROWS + row;
     if (a.lse && qrow < a.B) a.lse[(size_t)h * a.B + qrow] = lse * kLn2;
   }
   __syncthreads();
-  for (int e = tid; e < kTile * D / 4; e += 256) {
+  for (int e = tid; e < ROWS * D / 4; e += 256) {
     const int row = e / (D / 4), d4 = (e % (D / 4)) * 4;
-    const int qrow = qt * kTile + row;
+    const int qrow = qt * ROWS + row;
     if (qrow >= a.B) continue;
     float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
     for (int p = 0; p < S; ++p) {
-      const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((p0 + p) * kTile + row) * D + d4);
+      const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((p0 + p) * ROWS + row) * D + d4);
       const float wp = w[p][row];
       o0 = fmaf(wp, v.x, o0);
       o1 = fmaf(wp, v.y, o1);
@@ -450,6 +492,11 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
+#ifndef SWATTN_DENSE_NQ
+#define SWATTN_DENSE_NQ 1
+#endif
+constexpr int kDenseNQ = SWATTN_DENSE_NQ;
+
 hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const void* q,
                          const SlotPtrs* slots, int n_slots, const int32_t* tile_idx, int k_row,
                          void* out, float* lse, const SplitPlan& plan, hipStream_t stream) {
@@ -472,29 +519,34 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
   a.part_o = plan.part_o;
   a.part_lse = plan.part_lse;
   for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0};
-  const int tiles = g.nt * g.H;
   if (bf16) {
     if (g.d != 128) return hipErrorInvalidValue;
     if (tile_idx) {
-      a.n_full = tiles;
+      a.n_qt = g.nt;
+      a.n_full = g.nt * g.H;
       a.n_split = 0;
-      hipLaunchKernelGGL((attend_bf16_kernel<true>), dim3(tiles), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attend_bf16_kernel<true, 1>), dim3(a.n_full), dim3(256), 0, stream, a);
       return hipGetLastError();
     }
-    // tail split: whole rounds of `slots` workgroups own whole tiles; the tiles of a last,
+    constexpr int NQ = kDenseNQ;
+    constexpr int ROWS = 128 * NQ;
+    a.n_qt = (g.B + ROWS - 1) / ROWS;
+    const int tiles = a.n_qt * g.H;
+    // tail split: whole rounds of resident workgroups own whole tiles; the tiles of a last,
     // partial round are cut into up to kMaxSplit key ranges (only when a whole round exists)
-    const int conc = plan.concurrent;
+    const int conc = NQ == 1 ? 2 * plan.cus : plan.cus;   // workgroups resident at once
+    const int max_pieces = plan.max_rows / ROWS;
     const int tail = conc > 0 ? tiles % conc : 0;
     int split = 0;
     if (plan.part_o && conc > 0 && tiles >= conc && tail > 0) {
-      split = std::min(std::min(kMaxSplit, conc / tail), plan.max_pieces / tail);
+      split = std::min(std::min(kMaxSplit, conc / tail), max_pieces / tail);
       split = std::min(split, n_slots * ((g.B + KB - 1) / KB));   // no empty key ranges
       if (split < 2) split = 0;
     }
     a.n_full = split ? tiles - tail : tiles;
     a.n_split = split;
-    hipLaunchKernelGGL((attend_bf16_kernel<false>), dim3(a.n_full + tail * split), dim3(256), 0, stream, a);
-    if (split) hipLaunchKernelGGL(merge_kernel, dim3(tail), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<false, NQ>), dim3(a.n_full + tail * split), dim3(256), 0, stream, a);
+    if (split) hipLaunchKernelGGL((merge_kernel<ROWS>), dim3(tail), dim3(256), 0, stream, a);
   } else {
     if (tile_idx) return hipErrorInvalidValue;
     const dim3 grid((g.B + 63) / 64, g.H), block(64);

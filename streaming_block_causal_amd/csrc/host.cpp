@@ -124,8 +124,8 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
   L->table_floats = 2 * ((size_t)L->t_len * L->pt + (size_t)g.lat_h * L->ph + (size_t)g.lat_w * L->pw);
   const int copies = c.twin ? 2 : 1;
   L->ws_bytes = c.dtype == SW_BF16
-                    ? align256((size_t)kMaxPieces * kTile * g.d * sizeof(float)) +
-                          align256((size_t)kMaxPieces * kTile * sizeof(float))
+                    ? align256((size_t)kSplitRows * g.d * sizeof(float)) +
+                          align256((size_t)kSplitRows * sizeof(float))
                     : 0;
   L->total = (size_t)L->P * copies * (2 * L->kv_bytes + L->pooled_bytes) +
              align256(L->table_floats * sizeof(float)) + L->ws_bytes;
@@ -261,9 +261,9 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
     float* tab = reinterpret_cast<float*>(p);
     p += align256(L.table_floats * sizeof(float));
     c->plan.part_o = L.ws_bytes ? reinterpret_cast<float*>(p) : nullptr;
-    c->plan.part_lse = L.ws_bytes ? reinterpret_cast<float*>(p + align256((size_t)kMaxPieces * kTile * L.g.d * sizeof(float)))
+    c->plan.part_lse = L.ws_bytes ? reinterpret_cast<float*>(p + align256((size_t)kSplitRows * L.g.d * sizeof(float)))
                                   : nullptr;
-    c->plan.max_pieces = L.ws_bytes ? kMaxPieces : 0;
+    c->plan.max_rows = L.ws_bytes ? kSplitRows : 0;
     int dev = 0, cus = 0;
     hipError_t de = hipGetDevice(&dev);
     if (de == hipSuccess) de = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -271,7 +271,7 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
       delete c;
       return hip_fail(de, "device query");
     }
-    c->plan.concurrent = 2 * cus;   // the dense attention kernel runs two workgroups per CU
+    c->plan.cus = cus;
     std::vector<float> host;
     fill_tables(L, cfg->rope_theta, host);
     hipError_t e = hipMemsetAsync(c->pool, 0, L.total, c->stream);

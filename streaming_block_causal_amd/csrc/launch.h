@@ -38,15 +38,15 @@ hipError_t launch_append(const Geometry& g, const RopeTab& rt, bool bf16, const 
                          const void* v_raw, void* k_dst, void* v_dst, float* pooled_dst,
                          hipStream_t stream);
 
-// Work split of the dense bf16 attention grid: `concurrent` = workgroups resident at once
-// (2 per CU); the workspace holds up to max_pieces partial 128-query results.
+// Work split of the dense bf16 attention grid: the device's CU count sets how many
+// workgroups are resident at once; the workspace holds max_rows partial query rows.
 struct SplitPlan {
-  int concurrent;
-  int max_pieces;
-  float* part_o;     // [max_pieces][128][128]
-  float* part_lse;   // [max_pieces][128]
+  int cus;
+  int max_rows;
+  float* part_o;     // [max_rows][d]
+  float* part_lse;   // [max_rows]
 };
-constexpr int kMaxPieces = 512;
+constexpr int kSplitRows = 512 * 128;
 
 // K2 / K3: chunk attention over the given slots (logical order); tile_idx == nullptr -> dense.
 hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const void* q,
