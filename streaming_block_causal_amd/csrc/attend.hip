@@ -127,12 +127,13 @@ __device__ __forceinline__ bool block_at(const int32_t* list, int n_slots, int n
 // XOR-swizzled so the MFMA operand reads are bank-conflict free:
 //   K  [64 keys][128 dims]: row r at r * 256 B, 16-byte chunk c at slot c ^ (r & 15)
 //   V^T[128 dims][64 keys]: row d at d * 128 B, 16-byte chunk c at slot c ^ ((d >> 1) & 7)
-// A workgroup's 4 waves each issue 4 K and 4 V instructions (1 KB each) per block.
+// A workgroup's NW waves each issue 16/NW K and 16/NW V instructions (1 KB each) per block.
+template <int NW>
 __device__ __forceinline__ void stage_block(const u16* kbase, const u16* vbase, int n_pad, int wave, int lane,
                                             u16* kdst, u16* vdst) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int C = 4 * i + wave;   // 1 KB chunk of the block
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int C = NW * i + wave;   // 1 KB chunk of the block
     const int r = 4 * C + (lane >> 4), ck = (lane & 15) ^ (r & 15);
     __builtin_amdgcn_global_load_lds(
         reinterpret_cast<const __attribute__((address_space(1))) void*>(
@@ -148,22 +149,23 @@ __device__ __forceinline__ void stage_block(const u16* kbase, const u16* vbase, 
   }
 }
 
-// One workgroup = 4 waves = 128 queries of one head (32 per wave); two workgroups share a CU
-// (<= 256 registers per wave, 64 KB of LDS each).  The K/V blocks a workgroup streams are shared
-// by its waves through LDS: while block n is computed from one buffer, block n+1 is already
-// landing in the other; one barrier per block.
+// One workgroup = NW waves = 32 * NW queries of one head (32 per wave), two waves per SIMD:
+// NW = 4 -> two workgroups per CU, NW = 8 -> one.  The K/V blocks a workgroup streams are shared
+// by its waves through a ring of ST LDS buffers: block n + ST - 1 is requested while block n is
+// computed; one barrier per block.
 // Workgroups past n_full each take 1/n_split of the key blocks of one of the remaining tiles
 // and write a normalised partial result; merge_kernel combines them.  This fills the last,
 // partial round of the grid instead of leaving most CUs idle.
-template <bool SPARSE, int NQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <bool SPARSE, int NW, int ST>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_bf16_kernel(AttnArgs a) {
-  static_assert(NQ == 1, "one 32-query sub-tile per wave");
-  constexpr int ROWS = 128;
+  constexpr int ROWS = 32 * NW;
   __shared__ __attribute__((aligned(1024))) u16 ks0[KB * D];
   __shared__ __attribute__((aligned(1024))) u16 ks1[KB * D];
+  __shared__ __attribute__((aligned(1024))) u16 ks2[ST > 2 ? KB * D : 8];
   __shared__ __attribute__((aligned(1024))) u16 vs0[D * KB];
   __shared__ __attribute__((aligned(1024))) u16 vs1[D * KB];
+  __shared__ __attribute__((aligned(1024))) u16 vs2[ST > 2 ? D * KB : 8];
   __shared__ SlotPtrs sslot[kMaxSlots];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -218,13 +220,12 @@ void attend_bf16_kernel(AttnArgs a) {
   const int32_t* list = SPARSE ? a.tile_idx + ((size_t)h * nt + qt) * a.k_row : nullptr;
 
   auto stage = [&](int s, int kb, u16* kdst, u16* vdst) {
-    stage_block(static_cast<const u16*>(sslot[s].k) + h * kstride + (size_t)kb * KB * D,
-                static_cast<const u16*>(sslot[s].v) + h * kstride + kb * KB, n_pad, wave, lane, kdst, vdst);
+    stage_block<NW>(static_cast<const u16*>(sslot[s].k) + h * kstride + (size_t)kb * KB * D,
+                    static_cast<const u16*>(sslot[s].v) + h * kstride + kb * KB, n_pad, wave, lane, kdst, vdst);
   };
 
-  auto compute = [&](const u16* kl, const u16* vl, int kb) {
-    // ---- S^T = K Q^T for 64 keys: two 32x32 tiles, lane holds 16 keys of query ln
-    f32x16 s0, s1;
+  // ---- S^T = K Q^T for 64 keys: two 32x32 tiles, lane holds 16 keys of query ln
+  auto qk = [&](const u16* kl, int kb, f32x16& s0, f32x16& s1) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] = 0.f;
@@ -264,7 +265,9 @@ void attend_bf16_kernel(AttnArgs a) {
         if (key + 32 >= kvalid) s1[r] = -INFINITY;
       }
     }
-    // ---- online softmax (log2 domain, lazy rescale)
+  };
+  // ---- online softmax (log2 domain, lazy rescale), then O^T += V^T P^T
+  auto sm_pv = [&](const u16* vl, f32x16& s0, f32x16& s1) {
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
@@ -306,33 +309,83 @@ void attend_bf16_kernel(AttnArgs a) {
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[g], acc[t], 0, 0, 0);
       }
   };
+  f32x16 s0, s1;
 
-  int i = i0, sl = 0, kb = 0;
-  while (i < i1 && !block_at(list, n_slots, nt, nkb, i, sl, kb)) ++i;
-  if (i < i1) stage(sl, kb, ks0, vs0);
+  // schedule positions of the block being computed (i) and of the ST - 1 blocks in flight
+  int pos[ST], bsl[ST], bkb[ST];
+  {
+    int q = i0;
+#pragma unroll
+    for (int u = 0; u < ST; ++u) {
+      while (q < i1 && !block_at(list, n_slots, nt, nkb, q, bsl[u], bkb[u])) ++q;
+      pos[u] = q;
+      if (q < i1) ++q;
+    }
+  }
+  u16* const kbuf[3] = {ks0, ks1, ks2};
+  u16* const vbuf[3] = {vs0, vs1, vs2};
+#pragma unroll
+  for (int u = 0; u < ST - 1; ++u)
+    if (pos[u] < i1) stage(bsl[u], bkb[u], kbuf[u], vbuf[u]);
   int cur_slot = -1;
 
-  // one pipeline step: block (sl, kb) is in (kc, vc); the next one goes to (kn, vn)
+  // one pipeline step: compute the block in buffer C while block (n + ST - 1) lands in buffer N
   auto step = [&](const u16* kc, const u16* vc, u16* kn, u16* vn) {
-    int j = i + 1, nsl = 0, nkb2 = 0;
-    while (j < i1 && !block_at(list, n_slots, nt, nkb, j, nsl, nkb2)) ++j;
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of block i has landed
-    __syncthreads();                      // ... and everyone's; buffer (kn, vn) is free again
-    if (j < i1) stage(nsl, nkb2, kn, vn);
+    const int sl = bsl[0], kb = bkb[0];
+    // this wave's loads of the block in C have landed when at most the newer groups remain
+    if (ST == 3 && pos[1] < i1)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * 16 / NW));   // vmcnt(2*16/NW)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+    // ... and everyone's have; buffer N (block n - 1) is no longer read: its LDS reads were
+    // consumed by that block's MFMAs.  A bare s_barrier: __syncthreads() would also wait for
+    // the newer blocks still in flight.  The empty asm keeps the compiler from moving memory
+    // accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // find the next block past the last one in flight
+    int q = pos[ST - 1] < i1 ? pos[ST - 1] + 1 : i1, nsl = 0, nkb2 = 0;
+    if (pos[ST - 1] < i1) {
+      while (q < i1 && !block_at(list, n_slots, nt, nkb, q, nsl, nkb2)) ++q;
+    }
+    if (ST == 2) {
+      if (pos[1] < i1) stage(bsl[1], bkb[1], kn, vn);
+    } else {
+      if (pos[ST - 1] < i1) stage(bsl[ST - 1], bkb[ST - 1], kn, vn);
+    }
     if (sl != cur_slot) {
       cur_slot = sl;
       load_q<0, kTimeJ>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, qb);
     }
-    compute(kc, vc, kb);
-    i = j;
-    sl = nsl;
-    kb = nkb2;
+    qk(kc, kb, s0, s1);
+    sm_pv(vc, s0, s1);
+#pragma unroll
+    for (int u = 0; u < ST - 1; ++u) {
+      pos[u] = pos[u + 1];
+      bsl[u] = bsl[u + 1];
+      bkb[u] = bkb[u + 1];
+    }
+    pos[ST - 1] = q;
+    bsl[ST - 1] = nsl;
+    bkb[ST - 1] = nkb2;
   };
-  while (i < i1) {
-    step(ks0, vs0, ks1, vs1);
-    if (i >= i1) break;
-    step(ks1, vs1, ks0, vs0);
+  if (ST == 2) {
+    while (pos[0] < i1) {
+      step(ks0, vs0, ks1, vs1);
+      if (pos[0] >= i1) break;
+      step(ks1, vs1, ks0, vs0);
+    }
+  } else {
+    while (pos[0] < i1) {
+      step(ks0, vs0, ks2, vs2);
+      if (pos[0] >= i1) break;
+      step(ks1, vs1, ks0, vs0);
+      if (pos[0] >= i1) break;
+      step(ks2, vs2, ks1, vs1);
+    }
   }
+
 
   const float l_tot = swap_halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // an empty key range contributes nothing
@@ -492,10 +545,15 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-#ifndef SWATTN_DENSE_NQ
-#define SWATTN_DENSE_NQ 1
+#ifndef SWATTN_DENSE_WAVES
+#define SWATTN_DENSE_WAVES 8
 #endif
-constexpr int kDenseNQ = SWATTN_DENSE_NQ;
+#ifndef SWATTN_STAGES
+#define SWATTN_STAGES 2
+#endif
+constexpr int kDenseWaves = SWATTN_DENSE_WAVES;
+constexpr int kDenseStages = SWATTN_STAGES;
+
 
 hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const void* q,
                          const SlotPtrs* slots, int n_slots, const int32_t* tile_idx, int k_row,
@@ -525,16 +583,16 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
       a.n_qt = g.nt;
       a.n_full = g.nt * g.H;
       a.n_split = 0;
-      hipLaunchKernelGGL((attend_bf16_kernel<true, 1>), dim3(a.n_full), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attend_bf16_kernel<true, 4, 2>), dim3(a.n_full), dim3(256), 0, stream, a);
       return hipGetLastError();
     }
-    constexpr int NQ = kDenseNQ;
-    constexpr int ROWS = 128 * NQ;
+    constexpr int NW = kDenseWaves, ST = kDenseStages;
+    constexpr int ROWS = 32 * NW;
     a.n_qt = (g.B + ROWS - 1) / ROWS;
     const int tiles = a.n_qt * g.H;
     // tail split: whole rounds of resident workgroups own whole tiles; the tiles of a last,
     // partial round are cut into up to kMaxSplit key ranges (only when a whole round exists)
-    const int conc = NQ == 1 ? 2 * plan.cus : plan.cus;   // workgroups resident at once
+    const int conc = NW == 4 ? 2 * plan.cus : plan.cus;   // workgroups resident at once
     const int max_pieces = plan.max_rows / ROWS;
     const int tail = conc > 0 ? tiles % conc : 0;
     int split = 0;
@@ -545,7 +603,8 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
     }
     a.n_full = split ? tiles - tail : tiles;
     a.n_split = split;
-    hipLaunchKernelGGL((attend_bf16_kernel<false, NQ>), dim3(a.n_full + tail * split), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<false, NW, ST>), dim3(a.n_full + tail * split), dim3(64 * NW), 0,
+                       stream, a);
     if (split) hipLaunchKernelGGL((merge_kernel<ROWS>), dim3(tail), dim3(256), 0, stream, a);
   } else {
     if (tile_idx) return hipErrorInvalidValue;
