@@ -72,6 +72,7 @@ constexpr int KB = 64;          // keys per LDS block
 constexpr int KS = D + 8;       // LDS row stride of K (bf16 elements)
 constexpr int VS = KB + 8;      // LDS row stride of V^T
 constexpr float kRescaleSlack = 8.0f;
+
 #ifndef QK_AHEAD
 #define QK_AHEAD 2
 #endif   // log2 units: exp2 arguments stay <= 8 between rescales
@@ -151,21 +152,19 @@ __device__ __forceinline__ void stage_block(const u16* kbase, const u16* vbase, 
 
 // One workgroup = NW waves = 32 * NW queries of one head (32 per wave), two waves per SIMD:
 // NW = 4 -> two workgroups per CU, NW = 8 -> one.  The K/V blocks a workgroup streams are shared
-// by its waves through a ring of ST LDS buffers: block n + ST - 1 is requested while block n is
-// computed; one barrier per block.
+// by its waves through two LDS buffers: block n + 1 is requested while block n is computed; one
+// barrier per block.
 // Workgroups past n_full each take 1/n_split of the key blocks of one of the remaining tiles
 // and write a normalised partial result; merge_kernel combines them.  This fills the last,
 // partial round of the grid instead of leaving most CUs idle.
-template <bool SPARSE, int NW, int ST>
+template <bool SPARSE, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_bf16_kernel(AttnArgs a) {
   constexpr int ROWS = 32 * NW;
   __shared__ __attribute__((aligned(1024))) u16 ks0[KB * D];
   __shared__ __attribute__((aligned(1024))) u16 ks1[KB * D];
-  __shared__ __attribute__((aligned(1024))) u16 ks2[ST > 2 ? KB * D : 8];
   __shared__ __attribute__((aligned(1024))) u16 vs0[D * KB];
   __shared__ __attribute__((aligned(1024))) u16 vs1[D * KB];
-  __shared__ __attribute__((aligned(1024))) u16 vs2[ST > 2 ? D * KB : 8];
   __shared__ SlotPtrs sslot[kMaxSlots];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -218,6 +217,7 @@ void attend_bf16_kernel(AttnArgs a) {
 
   const size_t kstride = (size_t)n_pad * D;   // per head, K and V^T alike
   const int32_t* list = SPARSE ? a.tile_idx + ((size_t)h * nt + qt) * a.k_row : nullptr;
+
 
   auto stage = [&](int s, int kb, u16* kdst, u16* vdst) {
     stage_block<NW>(static_cast<const u16*>(sslot[s].k) + h * kstride + (size_t)kb * KB * D,
@@ -311,49 +311,35 @@ void attend_bf16_kernel(AttnArgs a) {
   };
   f32x16 s0, s1;
 
-  // schedule positions of the block being computed (i) and of the ST - 1 blocks in flight
-  int pos[ST], bsl[ST], bkb[ST];
+  // schedule positions: p[0] computed, p[1] staged, p[2] looked up ahead
+  int pos[3], bsl[3], bkb[3];
   {
     int q = i0;
 #pragma unroll
-    for (int u = 0; u < ST; ++u) {
+    for (int u = 0; u < 3; ++u) {
       while (q < i1 && !block_at(list, n_slots, nt, nkb, q, bsl[u], bkb[u])) ++q;
       pos[u] = q;
       if (q < i1) ++q;
     }
   }
-  u16* const kbuf[3] = {ks0, ks1, ks2};
-  u16* const vbuf[3] = {vs0, vs1, vs2};
-#pragma unroll
-  for (int u = 0; u < ST - 1; ++u)
-    if (pos[u] < i1) stage(bsl[u], bkb[u], kbuf[u], vbuf[u]);
+  if (pos[0] < i1) stage(bsl[0], bkb[0], ks0, vs0);
   int cur_slot = -1;
 
-  // one pipeline step: compute the block in buffer C while block (n + ST - 1) lands in buffer N
+  // one pipeline step: compute the block in buffer C while block n + 1 lands in buffer N
   auto step = [&](const u16* kc, const u16* vc, u16* kn, u16* vn) {
     const int sl = bsl[0], kb = bkb[0];
-    // this wave's loads of the block in C have landed when at most the newer groups remain
-    if (ST == 3 && pos[1] < i1)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * 16 / NW));   // vmcnt(2*16/NW)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
-    // ... and everyone's have; buffer N (block n - 1) is no longer read: its LDS reads were
-    // consumed by that block's MFMAs.  A bare s_barrier: __syncthreads() would also wait for
-    // the newer blocks still in flight.  The empty asm keeps the compiler from moving memory
-    // accesses across it.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of block n has landed
+    // ... and everyone's has; buffer N (block n - 1) is no longer read: its LDS reads were
+    // consumed by that block's MFMAs.  A bare s_barrier, the empty asm keeps the compiler from
+    // moving memory accesses across it.
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // find the next block past the last one in flight
-    int q = pos[ST - 1] < i1 ? pos[ST - 1] + 1 : i1, nsl = 0, nkb2 = 0;
-    if (pos[ST - 1] < i1) {
+    int q = pos[2] < i1 ? pos[2] + 1 : i1, nsl = 0, nkb2 = 0;
+    if (pos[2] < i1) {
       while (q < i1 && !block_at(list, n_slots, nt, nkb, q, nsl, nkb2)) ++q;
     }
-    if (ST == 2) {
-      if (pos[1] < i1) stage(bsl[1], bkb[1], kn, vn);
-    } else {
-      if (pos[ST - 1] < i1) stage(bsl[ST - 1], bkb[ST - 1], kn, vn);
-    }
+    if (pos[1] < i1) stage(bsl[1], bkb[1], kn, vn);
     if (sl != cur_slot) {
       cur_slot = sl;
       load_q<0, kTimeJ>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, qb);
@@ -361,31 +347,20 @@ void attend_bf16_kernel(AttnArgs a) {
     qk(kc, kb, s0, s1);
     sm_pv(vc, s0, s1);
 #pragma unroll
-    for (int u = 0; u < ST - 1; ++u) {
+    for (int u = 0; u < 2; ++u) {
       pos[u] = pos[u + 1];
       bsl[u] = bsl[u + 1];
       bkb[u] = bkb[u + 1];
     }
-    pos[ST - 1] = q;
-    bsl[ST - 1] = nsl;
-    bkb[ST - 1] = nkb2;
+    pos[2] = q;
+    bsl[2] = nsl;
+    bkb[2] = nkb2;
   };
-  if (ST == 2) {
-    while (pos[0] < i1) {
-      step(ks0, vs0, ks1, vs1);
-      if (pos[0] >= i1) break;
-      step(ks1, vs1, ks0, vs0);
-    }
-  } else {
-    while (pos[0] < i1) {
-      step(ks0, vs0, ks2, vs2);
-      if (pos[0] >= i1) break;
-      step(ks1, vs1, ks0, vs0);
-      if (pos[0] >= i1) break;
-      step(ks2, vs2, ks1, vs1);
-    }
+  while (pos[0] < i1) {
+    step(ks0, vs0, ks1, vs1);
+    if (pos[0] >= i1) break;
+    step(ks1, vs1, ks0, vs0);
   }
-
 
   const float l_tot = swap_halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // an empty key range contributes nothing
@@ -548,11 +523,9 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
 #ifndef SWATTN_DENSE_WAVES
 #define SWATTN_DENSE_WAVES 8
 #endif
-#ifndef SWATTN_STAGES
-#define SWATTN_STAGES 2
-#endif
+
 constexpr int kDenseWaves = SWATTN_DENSE_WAVES;
-constexpr int kDenseStages = SWATTN_STAGES;
+
 
 
 hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const void* q,
@@ -579,32 +552,36 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
   for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0};
   if (bf16) {
     if (g.d != 128) return hipErrorInvalidValue;
-    if (tile_idx) {
+    // tail split: whole rounds of resident workgroups own whole tiles; the tiles of a last,
+    // partial round are cut into up to kMaxSplit key ranges (only when a whole round exists)
+    auto plan_split = [&](int tiles, int conc, int rows, int blocks) {
+      const int tail = conc > 0 ? tiles % conc : 0;
+      int split = 0;
+      if (plan.part_o && conc > 0 && tiles >= conc && tail > 0) {
+        split = std::min(std::min(kMaxSplit, conc / tail), (plan.max_rows / rows) / tail);
+        split = std::min(split, blocks);   // no empty key ranges
+        if (split < 2) split = 0;
+      }
+      a.n_full = split ? tiles - tail : tiles;
+      a.n_split = split;
+      return tail;
+    };
+    if (tile_idx) {   // block-sparse: 128-query tiles, 4 waves, two workgroups per CU (no split:
+                      // the lists are short and the merge costs more than the tail round)
       a.n_qt = g.nt;
       a.n_full = g.nt * g.H;
       a.n_split = 0;
-      hipLaunchKernelGGL((attend_bf16_kernel<true, 4, 2>), dim3(a.n_full), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attend_bf16_kernel<true, 4>), dim3(a.n_full), dim3(256), 0, stream, a);
       return hipGetLastError();
     }
-    constexpr int NW = kDenseWaves, ST = kDenseStages;
+    constexpr int NW = kDenseWaves;
     constexpr int ROWS = 32 * NW;
     a.n_qt = (g.B + ROWS - 1) / ROWS;
-    const int tiles = a.n_qt * g.H;
-    // tail split: whole rounds of resident workgroups own whole tiles; the tiles of a last,
-    // partial round are cut into up to kMaxSplit key ranges (only when a whole round exists)
     const int conc = NW == 4 ? 2 * plan.cus : plan.cus;   // workgroups resident at once
-    const int max_pieces = plan.max_rows / ROWS;
-    const int tail = conc > 0 ? tiles % conc : 0;
-    int split = 0;
-    if (plan.part_o && conc > 0 && tiles >= conc && tail > 0) {
-      split = std::min(std::min(kMaxSplit, conc / tail), max_pieces / tail);
-      split = std::min(split, n_slots * ((g.B + KB - 1) / KB));   // no empty key ranges
-      if (split < 2) split = 0;
-    }
-    a.n_full = split ? tiles - tail : tiles;
-    a.n_split = split;
-    hipLaunchKernelGGL((attend_bf16_kernel<false, NW, ST>), dim3(a.n_full + tail * split), dim3(64 * NW), 0,
-                       stream, a);
+    const int tail = plan_split(a.n_qt * g.H, conc, ROWS, n_slots * ((g.B + KB - 1) / KB));
+    const int split = a.n_split;
+    hipLaunchKernelGGL((attend_bf16_kernel<false, NW>), dim3(a.n_full + tail * split), dim3(64 * NW), 0, stream,
+                       a);
     if (split) hipLaunchKernelGGL((merge_kernel<ROWS>), dim3(tail), dim3(256), 0, stream, a);
   } else {
     if (tile_idx) return hipErrorInvalidValue;

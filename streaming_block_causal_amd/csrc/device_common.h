@@ -9,6 +9,7 @@
 namespace swattn {
 
 typedef uint16_t u16;
+typedef uint32_t u32;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
