@@ -34,7 +34,7 @@ struct MaskArgs {
 
 __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   constexpr int D = 128;
-  __shared__ float red[4][D];
+  __shared__ float red[16][D];
   __shared__ float qs[kMaxSlots][D];
   __shared__ float sc[kMaxKeyTiles];
   __shared__ unsigned char keep[kMaxKeyTiles];
@@ -52,31 +52,50 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
     }
   const RopeTab rt = a.rt;
 
-  // 1. mean over the tile's valid queries of q rotated at block-local positions
+  // 1. mean over the tile's valid queries of q rotated at block-local positions.  Thread t takes
+  //    4 pairs (16 bytes) of 8 rows; all loads are issued before any is used.
   {
-    const int p = tid & 63, rg = tid >> 6;
-    float s0 = 0.f, s1 = 0.f;
-    for (int i = 0; i < kTile / 4; ++i) {
-      const int r = qt * kTile + rg + 4 * i;
-      if (r >= a.B) break;
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(a.q + ((size_t)r * a.H + h) * D + 2 * p);
-      const int f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
-      float c, s;
-      rope_cs(rt, p, f, hh, ww, c, s);
-      const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
-      s0 += x0 * c - x1 * s;
-      s1 += x0 * s + x1 * c;
+    const int pg = tid & 15, rg = tid >> 4;   // pair group (4 pairs), row group
+    float acc8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
+    uint4 raw[8];
+    int rows[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      rows[i] = qt * kTile + rg + 16 * i;
+      raw[i] = rows[i] < a.B ? ldg16(a.q + ((size_t)rows[i] * a.H + h) * D + 8 * pg) : make_uint4(0, 0, 0, 0);
     }
-    red[rg][2 * p] = s0;
-    red[rg][2 * p + 1] = s1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (rows[i] >= a.B) continue;
+      const int r = rows[i], f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float c, sn;
+        rope_cs(rt, 4 * pg + e, f, hh, ww, c, sn);
+        const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xffff0000u);
+        acc8[2 * e] += x0 * c - x1 * sn;
+        acc8[2 * e + 1] += x0 * sn + x1 * c;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rg][8 * pg + e] = acc8[e];
   }
   __syncthreads();
   // 2. relocate per slot: turn the time pairs by delta_l
   if (tid < D / 2) {
     const int p = tid;
     const float cnt = (float)min(kTile, a.B - qt * kTile);
-    const float x0 = (red[0][2 * p] + red[1][2 * p] + red[2][2 * p] + red[3][2 * p]) / cnt;
-    const float x1 = (red[0][2 * p + 1] + red[1][2 * p + 1] + red[2][2 * p + 1] + red[3][2 * p + 1]) / cnt;
+    float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      x0 += red[g][2 * p];
+      x1 += red[g][2 * p + 1];
+    }
+    x0 /= cnt;
+    x1 /= cnt;
     for (int sl = 0; sl < a.n_slots; ++sl) {
       float c = 1.f, s = 0.f;
       if (p < rt.pt) {
@@ -116,6 +135,7 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
     } else {
       const float su = sc[u];
       int rank = 0;
+#pragma unroll 8
       for (int v = 0; v < n_kv; ++v) {
         if (v == f_sink || v == f_diag || v == u) continue;
         const float sv = sc[v];
