@@ -75,6 +75,9 @@ constexpr float kRescaleSlack = 8.0f;
 
 #ifndef QK_AHEAD
 #define QK_AHEAD 2
+#endif
+#ifndef PV_AHEAD
+#define PV_AHEAD 8
 #endif   // log2 units: exp2 arguments stay <= 8 between rescales
 
 // Q^T operand of one wave: lane (hf, ln) holds q[row][16j + 8hf + 0..7] for j in [J0, J1), rotated
@@ -128,26 +131,23 @@ __device__ __forceinline__ bool block_at(const int32_t* list, int n_slots, int n
 // XOR-swizzled so the MFMA operand reads are bank-conflict free:
 //   K  [64 keys][128 dims]: row r at r * 256 B, 16-byte chunk c at slot c ^ (r & 15)
 //   V^T[128 dims][64 keys]: row d at d * 128 B, 16-byte chunk c at slot c ^ ((d >> 1) & 7)
-// A workgroup's NW waves each issue 16/NW K and 16/NW V instructions (1 KB each) per block.
+// A workgroup's NW waves each issue 16/NW K and 16/NW V loads (1 KB each) per block: load p of a
+// wave is K chunk NW * (p / 2) + wave for even p, the V^T chunk for odd p.  st[p] is the lane's
+// element offset inside the block (K: row-major, V^T: row stride n_pad).
+__device__ __forceinline__ const u16* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const u16*>(((uint64_t)hi << 32) | lo);
+}
 template <int NW>
-__device__ __forceinline__ void stage_block(const u16* kbase, const u16* vbase, int n_pad, int wave, int lane,
-                                            u16* kdst, u16* vdst) {
-#pragma unroll
-  for (int i = 0; i < 16 / NW; ++i) {
-    const int C = NW * i + wave;   // 1 KB chunk of the block
-    const int r = 4 * C + (lane >> 4), ck = (lane & 15) ^ (r & 15);
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const __attribute__((address_space(1))) void*>(
-            reinterpret_cast<uintptr_t>(kbase + (size_t)r * D + 8 * ck)),
-        reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(kdst + C * 512)), 16,
-        0, 0);
-    const int d = 8 * C + (lane >> 3), cv = (lane & 7) ^ ((d >> 1) & 7);
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const __attribute__((address_space(1))) void*>(
-            reinterpret_cast<uintptr_t>(vbase + (size_t)d * n_pad + 8 * cv)),
-        reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(vdst + C * 512)), 16,
-        0, 0);
-  }
+__device__ __forceinline__ void stage_load(int p, const u16* kbase, const u16* vbase, const int (&st)[32 / NW],
+                                           int wave, u16* kdst, u16* vdst) {
+  const int C = NW * (p >> 1) + wave;   // 1 KB chunk of the block
+  const u16* src = ((p & 1) ? vbase : kbase) + (uint32_t)st[p];
+  u16* dst = ((p & 1) ? vdst : kdst) + C * 512;
+  __builtin_amdgcn_global_load_lds(
+      reinterpret_cast<const __attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(src)),
+      reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(dst)), 16, 0, 0);
 }
 
 // One workgroup = NW waves = 32 * NW queries of one head (32 per wave), two waves per SIMD:
@@ -161,13 +161,14 @@ template <bool SPARSE, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_bf16_kernel(AttnArgs a) {
   constexpr int ROWS = 32 * NW;
-  __shared__ __attribute__((aligned(1024))) u16 ks0[KB * D];
-  __shared__ __attribute__((aligned(1024))) u16 ks1[KB * D];
-  __shared__ __attribute__((aligned(1024))) u16 vs0[D * KB];
-  __shared__ __attribute__((aligned(1024))) u16 vs1[D * KB];
+  constexpr int NBUF = 2;
+  __shared__ __attribute__((aligned(1024))) u16 kbuf[NBUF][KB * D];
+  __shared__ __attribute__((aligned(1024))) u16 vbuf[NBUF][D * KB];
   __shared__ SlotPtrs sslot[kMaxSlots];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index made explicitly uniform: the LDS destinations of the staging loads (M0) then stay
+  // in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, ln = lane & 31;
   // the argument struct is never addressed (that would copy it to scratch): static indices only,
   // and every field the lambdas below need is copied to a local first
@@ -215,17 +216,38 @@ void attend_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) voff[g] = ln * 64 + 8 * ((2 * g + hf) ^ ((ln >> 1) & 7));
 
+  constexpr int NST = 32 / NW;   // staging loads per wave and block
+  int st[NST];
+#pragma unroll
+  for (int p = 0; p < NST; ++p) {
+    const int C = NW * (p >> 1) + wave;
+    if ((p & 1) == 0) {
+      const int r = 4 * C + (lane >> 4);
+      st[p] = r * D + 8 * ((lane & 15) ^ (r & 15));
+    } else {
+      const int d = 8 * C + (lane >> 3);
+      st[p] = d * n_pad + 8 * ((lane & 7) ^ ((d >> 1) & 7));
+    }
+  }
+
   const size_t kstride = (size_t)n_pad * D;   // per head, K and V^T alike
   const int32_t* list = SPARSE ? a.tile_idx + ((size_t)h * nt + qt) * a.k_row : nullptr;
 
-
-  auto stage = [&](int s, int kb, u16* kdst, u16* vdst) {
-    stage_block<NW>(static_cast<const u16*>(sslot[s].k) + h * kstride + (size_t)kb * KB * D,
-                    static_cast<const u16*>(sslot[s].v) + h * kstride + kb * KB, n_pad, wave, lane, kdst, vdst);
+  // global bases (uniform) of block kb of slot s; "no block" maps to block 0 of slot 0, a valid
+  // address whose reload into an unused buffer is harmless
+  auto block_base = [&](bool valid, int s, int kb, const u16*& kb_ptr, const u16*& vb_ptr) {
+    if (!valid) {
+      s = 0;
+      kb = 0;
+    }
+    const SlotPtrs sp = sslot[s];
+    kb_ptr = uniform_ptr(static_cast<const u16*>(sp.k) + h * kstride + (size_t)kb * KB * D);
+    vb_ptr = uniform_ptr(static_cast<const u16*>(sp.v) + h * kstride + kb * KB);
   };
 
   // ---- S^T = K Q^T for 64 keys: two 32x32 tiles, lane holds 16 keys of query ln
-  auto qk = [&](const u16* kl, int kb, f32x16& s0, f32x16& s1) {
+  auto qk = [&](const u16* kl, int kb, f32x16& s0, f32x16& s1, const u16* nkb, const u16* nvb, u16* kdst,
+                u16* vdst) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] = 0.f;
@@ -248,12 +270,16 @@ void attend_bf16_kernel(AttnArgs a) {
       }
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[jj % (QK_AHEAD + 1)][0], qb[jj], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[jj % (QK_AHEAD + 1)][1], qb[jj], s1, 0, 0, 0);
+      // the next block's staging loads ride along with the MFMAs instead of queueing up in the
+      // vector memory path right after the barrier
+      if (jj < NST) stage_load<NW>(jj, nkb, nvb, st, wave, kdst, vdst);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * QK_AHEAD, 0);   // the first reads
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       if (jj + QK_AHEAD < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next reads
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                         // two MFMAs
+      if (jj < NST) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // one staging load
     }
     __builtin_amdgcn_sched_barrier(0);
     const int kvalid = B - kb * KB;
@@ -268,6 +294,14 @@ void attend_bf16_kernel(AttnArgs a) {
   };
   // ---- online softmax (log2 domain, lazy rescale), then O^T += V^T P^T
   auto sm_pv = [&](const u16* vl, f32x16& s0, f32x16& s1) {
+    // V^T operands of the first PV_AHEAD MFMAs are requested before the softmax, so the P.V
+    // MFMAs find them in registers; MFMA i = (g, t) = (i / 4, i % 4) reads row block t, key group g
+    auto vread = [&](int i) { return *reinterpret_cast<const bf16x8*>(vl + 32 * (i & 3) * KB + voff[i >> 2]); };
+    bf16x8 vop[PV_AHEAD];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < PV_AHEAD; ++i) vop[i] = vread(i);
+    __builtin_amdgcn_sched_barrier(0);
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
@@ -302,12 +336,10 @@ void attend_bf16_kernel(AttnArgs a) {
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // ---- O^T += V^T P^T
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vl + 32 * t * KB + voff[g]);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[g], acc[t], 0, 0, 0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i % PV_AHEAD], pb[i >> 2], acc[i & 3], 0, 0, 0);
+      if (i + PV_AHEAD < 16) vop[i % PV_AHEAD] = vread(i + PV_AHEAD);
+    }
   };
   f32x16 s0, s1;
 
@@ -322,30 +354,44 @@ void attend_bf16_kernel(AttnArgs a) {
       if (q < i1) ++q;
     }
   }
-  if (pos[0] < i1) stage(bsl[0], bkb[0], ks0, vs0);
+  const u16 *nk, *nv;   // bases of the block staged next
+  if (pos[0] < i1) {
+    block_base(true, bsl[0], bkb[0], nk, nv);
+#pragma unroll
+    for (int p = 0; p < NST; ++p) stage_load<NW>(p, nk, nv, st, wave, kbuf[0], vbuf[0]);
+  }
+  block_base(pos[1] < i1, bsl[1], bkb[1], nk, nv);
   int cur_slot = -1;
+  bool pend = false;   // scores of the previous block wait for softmax and P.V
+  int pend_buf = 0;
 
-  // one pipeline step: compute the block in buffer C while block n + 1 lands in buffer N
-  auto step = [&](const u16* kc, const u16* vc, u16* kn, u16* vn) {
+  // one pipeline step: softmax and P.V of block n - 1, the barrier of block n, then S of block n
+  // from buffer cb while block n + 1 is requested into the next buffer
+  auto step = [&](const int cb) {
     const int sl = bsl[0], kb = bkb[0];
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of block n has landed
-    // ... and everyone's has; buffer N (block n - 1) is no longer read: its LDS reads were
-    // consumed by that block's MFMAs.  A bare s_barrier, the empty asm keeps the compiler from
-    // moving memory accesses across it.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    int q = pos[2] < i1 ? pos[2] + 1 : i1, nsl = 0, nkb2 = 0;
-    if (pos[2] < i1) {
-      while (q < i1 && !block_at(list, n_slots, nt, nkb, q, nsl, nkb2)) ++q;
-    }
-    if (pos[1] < i1) stage(bsl[1], bkb[1], kn, vn);
+    auto sync = [&]() {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of block n has landed
+      // ... and everyone's has; the buffer block n + 1 goes to (that of block n + 1 - NBUF) is
+      // no longer read: its LDS reads were consumed by that block's MFMAs before this barrier.  A
+      // bare s_barrier, the empty asm keeps the compiler from moving memory accesses across it.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    if (pend) sm_pv(vbuf[(cb + NBUF - 1) % NBUF], s0, s1);
+    sync();
     if (sl != cur_slot) {
       cur_slot = sl;
       load_q<0, kTimeJ>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, qb);
     }
-    qk(kc, kb, s0, s1);
-    sm_pv(vc, s0, s1);
+    qk(kbuf[cb], kb, s0, s1, nk, nv, kbuf[(cb + 1) % NBUF], vbuf[(cb + 1) % NBUF]);
+    pend = true;
+    pend_buf = cb;
+    // look the schedule up one block further while the MFMAs drain
+    int q = pos[2] < i1 ? pos[2] + 1 : i1, nsl = 0, nkb2 = 0;
+    if (pos[2] < i1) {
+      while (q < i1 && !block_at(list, n_slots, nt, nkb, q, nsl, nkb2)) ++q;
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       pos[u] = pos[u + 1];
@@ -355,12 +401,18 @@ void attend_bf16_kernel(AttnArgs a) {
     pos[2] = q;
     bsl[2] = nsl;
     bkb[2] = nkb2;
+    block_base(pos[1] < i1, bsl[1], bkb[1], nk, nv);
   };
   while (pos[0] < i1) {
-    step(ks0, vs0, ks1, vs1);
+    step(0);
     if (pos[0] >= i1) break;
-    step(ks1, vs1, ks0, vs0);
+    step(1);
   }
+  // the last step's staging loads (of a placeholder block when the range ended) must land before
+  // the workgroup's LDS can be handed to another workgroup
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // the last block's buffer is not restaged: no barrier needed before its P.V
+  if (pend) sm_pv(vbuf[pend_buf], s0, s1);
 
   const float l_tot = swap_halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // an empty key range contributes nothing
