@@ -82,7 +82,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20, help="timed chunks")
     ap.add_argument("--warmup", type=int, default=3, help="untimed chunks")
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle sample (0 = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=12,
+                    help="heads in the oracle sample, about 1 s of CPU time each at 540p (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (scales PMC byte counters)")
     args = ap.parse_args()
@@ -229,7 +230,8 @@ def main():
         "append_gbps": append_bytes / (avg_app * 1e-3) / 1e9,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(args.workload),
-                     "kernel": "attend_bf16_kernel<false>", "flops_per_launch": flops_call},
+                     "kernel": "attend_bf16_kernel<true, 4>" if w.sparse_keep else "attend_bf16_kernel<false, 8>",
+                     "flops_per_launch": flops_call},
     }
     if args.cpu_heads > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)

@@ -445,45 +445,38 @@ void attend_bf16_kernel(AttnArgs a) {
   }
 }
 
-// Combine the n_split partial results of each split tile: weights 2^(lse_p - lse), lse the
-// log2 sum of 2^lse_p over the pieces (the softmax normaliser of the whole key range).
+// Combine the n_split partial results of each split tile: weights 2^(lse_p - m) / sum, m the max
+// of the pieces' log2 sum-exp lse_p; the row's log2 sum-exp is m + log2(sum).  One workgroup per
+// (tile, 8 rows): thread (row, d4) reads its four dims of every piece once (HBM-bound).
 constexpr int kMaxSplit = 32;
+constexpr int kMergeRows = 8;
 template <int ROWS>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
-  __shared__ float w[kMaxSplit][ROWS];
   const int tid = threadIdx.x, S = a.n_split;
   const int tile = a.n_full + blockIdx.x;
   const int h = tile / a.n_qt, qt = tile - h * a.n_qt;
+  const int row = blockIdx.y * kMergeRows + (tid >> 5), d4 = (tid & 31) * 4;
+  const int qrow = qt * ROWS + row;
+  if (qrow >= a.B) return;
   const size_t p0 = (size_t)blockIdx.x * S;
-  for (int row = tid; row < ROWS; row += 256) {
-    float mx = -INFINITY;
-    for (int p = 0; p < S; ++p) mx = fmaxf(mx, a.part_lse[(p0 + p) * ROWS + row]);
-    float sum = 0.f;
-    for (int p = 0; p < S; ++p) sum += __builtin_amdgcn_exp2f(a.part_lse[(p0 + p) * ROWS + row] - mx);
-    const float lse = mx + __log2f(sum);
-    for (int p = 0; p < S; ++p) w[p][row] = __builtin_amdgcn_exp2f(a.part_lse[(p0 + p) * ROWS + row] - lse);
-    const int qrow = qt * ROWS + row;
-    if (a.lse && qrow < a.B) a.lse[(size_t)h * a.B + qrow] = lse * kLn2;
+  float mx = -INFINITY;
+  for (int p = 0; p < S; ++p) mx = fmaxf(mx, a.part_lse[(p0 + p) * ROWS + row]);
+  float sum = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  for (int p = 0; p < S; ++p) {
+    const float wp = __builtin_amdgcn_exp2f(a.part_lse[(p0 + p) * ROWS + row] - mx);
+    const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((p0 + p) * ROWS + row) * D + d4);
+    sum += wp;
+    o0 = fmaf(wp, v.x, o0);
+    o1 = fmaf(wp, v.y, o1);
+    o2 = fmaf(wp, v.z, o2);
+    o3 = fmaf(wp, v.w, o3);
   }
-  __syncthreads();
-  for (int e = tid; e < ROWS * D / 4; e += 256) {
-    const int row = e / (D / 4), d4 = (e % (D / 4)) * 4;
-    const int qrow = qt * ROWS + row;
-    if (qrow >= a.B) continue;
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    for (int p = 0; p < S; ++p) {
-      const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((p0 + p) * ROWS + row) * D + d4);
-      const float wp = w[p][row];
-      o0 = fmaf(wp, v.x, o0);
-      o1 = fmaf(wp, v.y, o1);
-      o2 = fmaf(wp, v.z, o2);
-      o3 = fmaf(wp, v.w, o3);
-    }
-    uint2 packed;
-    packed.x = (uint32_t)f2bf(o0) | ((uint32_t)f2bf(o1) << 16);
-    packed.y = (uint32_t)f2bf(o2) | ((uint32_t)f2bf(o3) << 16);
-    *reinterpret_cast<uint2*>(static_cast<u16*>(a.o) + ((size_t)qrow * a.H + h) * D + d4) = packed;
-  }
+  const float inv = 1.f / sum;
+  uint2 packed;
+  packed.x = (uint32_t)f2bf(o0 * inv) | ((uint32_t)f2bf(o1 * inv) << 16);
+  packed.y = (uint32_t)f2bf(o2 * inv) | ((uint32_t)f2bf(o3 * inv) << 16);
+  *reinterpret_cast<uint2*>(static_cast<u16*>(a.o) + ((size_t)qrow * a.H + h) * D + d4) = packed;
+  if (a.lse && d4 == 0) a.lse[(size_t)h * a.B + qrow] = (mx + __log2f(sum)) * kLn2;
 }
 
 // ------------------------------------------------------------------------------------
@@ -634,7 +627,7 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
     const int split = a.n_split;
     hipLaunchKernelGGL((attend_bf16_kernel<false, NW>), dim3(a.n_full + tail * split), dim3(64 * NW), 0, stream,
                        a);
-    if (split) hipLaunchKernelGGL((merge_kernel<ROWS>), dim3(tail), dim3(256), 0, stream, a);
+    if (split) hipLaunchKernelGGL((merge_kernel<ROWS>), dim3(tail, ROWS / kMergeRows), dim3(256), 0, stream, a);
   } else {
     if (tile_idx) return hipErrorInvalidValue;
     const dim3 grid((g.B + 63) / 64, g.H), block(64);
