@@ -70,7 +70,14 @@ def cpu_baseline(w, sample_heads):
     keys = (w.n_sink + w.n_window + 1) * w.block_tokens
     flops = attn_flops(w.block_tokens, sample_heads, w.head_dim, keys)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "nproc": os.cpu_count(),
             "sample": f"one steady-state call (chunk {n}, step 1), {sample_heads} of {w.n_heads} heads, "
                       f"all {w.block_tokens} queries x {keys} keys, fp64 numpy; {dt:.1f} s",
             "seconds": dt}
@@ -84,6 +91,8 @@ def main():
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-heads", type=int, default=12,
                     help="heads in the oracle sample, about 1 s of CPU time each at 540p (0 = skip)")
+    ap.add_argument("--flat-chunks", type=int, default=0, metavar="N",
+                    help="after the timed steps, time N more chunks one by one and report the latency slope")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (scales PMC byte counters)")
     args = ap.parse_args()
@@ -148,7 +157,7 @@ def main():
             cache.append("noisy", kn, vn, b)
         state["block"] += 1
 
-    ev = {"attn": [], "append": []}
+    ev = {"attn": [], "append": [], "mask": []}
     last_mask = {}
 
     def chunk(record):
@@ -156,7 +165,7 @@ def main():
         for s in range(T):
             q, k, v = sets[b % 2][s]
             if record:
-                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0, e1, em, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
                 e0.record(stream)
             cache.append("current", k, v, b)
             if record:
@@ -165,13 +174,18 @@ def main():
             if w.sparse_keep is not None:
                 idx, k_row = cache.build_tile_mask(q, w.sparse_keep)
                 last_mask["idx"] = idx
+                if record:
+                    em.record(stream)
                 cache.attend(q, step, tile_idx=idx, k_row=k_row, out=out)
             else:
+                if record:
+                    em.record(stream)
                 cache.attend(q, step, out=out)
             if record:
                 e2.record(stream)
                 ev["append"].append((e0, e1))
-                ev["attn"].append((e1, e2))
+                ev["mask"].append((e1, em))
+                ev["attn"].append((em, e2))
         commit()
 
     # fill the cache to steady state (appends and commits only, so every attention launch
@@ -190,7 +204,24 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
+    flat = None
+    if args.flat_chunks > 0:
+        # per-chunk latency over a long steady stream: least-squares slope vs chunk index
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.flat_chunks + 1)]
+        marks[0].record(stream)
+        for i in range(args.flat_chunks):
+            chunk(False)
+            marks[i + 1].record(stream)
+        torch.cuda.synchronize()
+        lat = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.flat_chunks)]
+        n = len(lat)
+        xm, ym = (n - 1) / 2.0, sum(lat) / n
+        slope = sum((i - xm) * (y - ym) for i, y in enumerate(lat)) / max(sum((i - xm) ** 2 for i in range(n)), 1e-30)
+        flat = {"chunks": n, "first_block": state["block"] - n, "mean_ms": ym,
+                "slope_pct_of_mean_per_100_chunks": 100.0 * slope * 100.0 / ym}
+
     attn_ms = [a.elapsed_time(b) for a, b in ev["attn"]]
+    mask_ms = [a.elapsed_time(b) for a, b in ev["mask"]]
     app_ms = [a.elapsed_time(b) for a, b in ev["append"]]
     keys = n_slots_full * B
     if w.sparse_keep is None:
@@ -204,6 +235,9 @@ def main():
     flops_chunk = flops_call * T
     ms_chunk = dt / args.steps * 1e3
     avg_attn = sum(attn_ms) / len(attn_ms)
+    avg_mask = sum(mask_ms) / len(mask_ms)
+    srt = sorted(attn_ms)
+    p50, p95 = srt[len(srt) // 2], srt[min(len(srt) - 1, int(0.95 * len(srt)))]
     achieved = flops_call / (avg_attn * 1e-3) / 1e12
     append_bytes = 2 * 2 * B * H * d * 2          # read raw K,V + write K,V (bf16)
     avg_app = sum(app_ms) / len(app_ms)
@@ -226,13 +260,28 @@ def main():
         "latent_frames_per_s": w.frames / (ms_chunk * 1e-3),
         "frac_of_bf16_peak_step": flops_chunk / (ms_chunk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "attention_ms_per_call": avg_attn,
+        "attention_ms_p50_p95": [p50, p95],
         "append_ms_per_call": avg_app,
         "append_gbps": append_bytes / (avg_app * 1e-3) / 1e9,
+        "latency_flatness": flat,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(args.workload),
                      "kernel": "attend_bf16_kernel<true, 4>" if w.sparse_keep else "attend_bf16_kernel<false, 8>",
                      "flops_per_launch": flops_call},
     }
+    if w.sparse_keep is not None:
+        # the mask reads Q once (plus the small pooled-key tables); the sparse attention's
+        # compulsory bytes are Q, O and the kept K/V tiles of every query tile
+        q_bytes = B * H * d * 2
+        idx = last_mask["idx"].long()
+        valid = torch.clamp(B - 128 * torch.arange(nt, device=dev), max=128).double()
+        kv_bytes = float((valid[idx % nt]).sum().item()) * d * 2 * 2
+        res["mask_ms_per_call"] = avg_mask
+        res["mask_gbps"] = q_bytes / (avg_mask * 1e-3) / 1e9
+        res["attention_ms_per_call_incl_mask"] = avg_attn + avg_mask
+        res["sparse_attention_hbm"] = {"bytes": 2 * q_bytes + kv_bytes,
+                                       "gbps": (2 * q_bytes + kv_bytes) / (avg_attn * 1e-3) / 1e9,
+                                       "frac": (2 * q_bytes + kv_bytes) / (avg_attn * 1e-3) / 1e9 / PEAK_HBM_GBPS}
     if args.cpu_heads > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
     else:
