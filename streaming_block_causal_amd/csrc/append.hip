@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < SUB; ++i) s += red[i][tid];
     const int cnt = min(kTile, a.B - j * kTile);
-    a.pooled[((size_t)h * a.nt + j) * D + tid] = s / (float)cnt;
+    a.pooled[((size_t)h * D + tid) * a.nt + j] = s / (float)cnt;   // [H][d][nt]: tiles contiguous
   }
 
   if (BF16) {

@@ -33,7 +33,7 @@ struct SlotPtrs {
 };
 
 // K1: rotate K at block-local positions, store K and V head-major, pad rows zeroed,
-// optional per-tile fp32 means of rotated K ([H][nt][d]).
+// optional per-tile fp32 means of rotated K ([H][d][nt]).
 hipError_t launch_append(const Geometry& g, const RopeTab& rt, bool bf16, const void* k_raw,
                          const void* v_raw, void* k_dst, void* v_dst, float* pooled_dst,
                          hipStream_t stream);

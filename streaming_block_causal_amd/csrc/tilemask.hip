@@ -34,10 +34,16 @@ struct MaskArgs {
 
 __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   constexpr int D = 128;
-  __shared__ float red[16][D];
-  __shared__ float qs[kMaxSlots][D];
-  __shared__ float sc[kMaxKeyTiles];
-  __shared__ unsigned char keep[kMaxKeyTiles];
+  // small LDS footprint (8 KB + the key-tile arrays sized at launch) so that many workgroups are
+  // resident and their latency-bound phases overlap: the partial sums of step 1 and the relocated
+  // queries of step 2 share one array
+  __shared__ float rq[16][D];
+  float (&red)[16][D] = rq;
+  float (&qs)[kMaxSlots][D] = rq;
+  extern __shared__ __attribute__((aligned(16))) float dyn[];   // sc[n_kv4], keep[n_kv4]
+  const int n_kv4 = (a.n_slots * a.nt + 3) & ~3;
+  float* sc = dyn;
+  unsigned char* keep = reinterpret_cast<unsigned char*>(dyn + n_kv4);
 
   __shared__ const float* spooled[kMaxSlots];
   __shared__ int sdelta[kMaxSlots];
@@ -84,11 +90,12 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
     for (int e = 0; e < 8; ++e) red[rg][8 * pg + e] = acc8[e];
   }
   __syncthreads();
-  // 2. relocate per slot: turn the time pairs by delta_l
+  // 2. relocate per slot: turn the time pairs by delta_l (the means are taken out of the shared
+  //    array before it is overwritten with the relocated queries)
+  const int p = tid;
+  float x0 = 0.f, x1 = 0.f;
   if (tid < D / 2) {
-    const int p = tid;
     const float cnt = (float)min(kTile, a.B - qt * kTile);
-    float x0 = 0.f, x1 = 0.f;
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       x0 += red[g][2 * p];
@@ -96,50 +103,59 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
     }
     x0 /= cnt;
     x1 /= cnt;
-    for (int sl = 0; sl < a.n_slots; ++sl) {
-      float c = 1.f, s = 0.f;
-      if (p < rt.pt) {
-        c = rt.cos_t[sdelta[sl] * rt.pt + p];
-        s = rt.sin_t[sdelta[sl] * rt.pt + p];
-      }
-      qs[sl][2 * p] = x0 * c - x1 * s;
-      qs[sl][2 * p + 1] = x0 * s + x1 * c;
+  }
+  // each pair's mean is broadcast through LDS, then thread (slot, pair) rotates it: all table
+  // loads of the step are issued at once
+  __shared__ float2 xm[D / 2];
+  if (tid < D / 2) xm[tid] = make_float2(x0, x1);
+  __syncthreads();
+  for (int idx = tid; idx < a.n_slots * (D / 2); idx += 256) {
+    const int sl = idx / (D / 2), pp = idx - sl * (D / 2);
+    float c = 1.f, sn = 0.f;
+    if (pp < rt.pt) {
+      c = rt.cos_t[sdelta[sl] * rt.pt + pp];
+      sn = rt.sin_t[sdelta[sl] * rt.pt + pp];
     }
+    const float2 m = xm[pp];
+    qs[sl][2 * pp] = m.x * c - m.y * sn;
+    qs[sl][2 * pp + 1] = m.x * sn + m.y * c;
   }
   __syncthreads();
-  // 3. scores of every key tile
-  for (int u = tid; u < n_kv; u += 256) {
-    const int sl = u / a.nt, jt = u - sl * a.nt;
-    const float4* kp = reinterpret_cast<const float4*>(spooled[sl] + ((size_t)h * a.nt + jt) * D);
-    float dot = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < D / 4; ++i) {
-      const float4 k4 = kp[i];
-      dot = fmaf(qs[sl][4 * i], k4.x, dot);
-      dot = fmaf(qs[sl][4 * i + 1], k4.y, dot);
-      dot = fmaf(qs[sl][4 * i + 2], k4.z, dot);
-      dot = fmaf(qs[sl][4 * i + 3], k4.w, dot);
-    }
-    sc[u] = dot * a.inv_sqrt_d;
-  }
-  __syncthreads();
-  // 4. forced tiles, then rank the rest: rank(u) = #better tiles (score, then lower index)
+  // 3. scores of every key tile: lane per tile, the pooled keys are stored dimension-major so a
+  //    wave's loads of one dimension are contiguous.  Forced tiles get -inf: they are kept
+  //    anyway and must not take a rank from the others.
   const int f_sink = a.has_sink ? 0 : -1;
   const int f_diag = (a.n_slots - 1) * a.nt + qt;
+  for (int u = tid; u < n_kv4; u += 256) {
+    float sv = -INFINITY;
+    if (u < n_kv && u != f_sink && u != f_diag) {
+      const int sl = u / a.nt, jt = u - sl * a.nt;
+      const float* kp = spooled[sl] + (size_t)h * D * a.nt + jt;
+      float dot = 0.f;
+#pragma unroll 16
+      for (int i = 0; i < D; ++i) dot = fmaf(qs[sl][i], kp[(size_t)i * a.nt], dot);
+      sv = dot * a.inv_sqrt_d;
+    }
+    sc[u] = sv;
+  }
+  __syncthreads();
+  // 4. rank of every other tile: rank(u) = #tiles with a higher score, ties to the lower index;
+  //    tile u is kept when its rank is below the budget left after the forced tiles.  The scores
+  //    are read four at a time (LDS broadcast), no branch per comparison.
   const int n_forced = 1 + (f_sink >= 0 ? 1 : 0);
   const int free_budget = a.k_row - n_forced;
   for (int u = tid; u < n_kv; u += 256) {
-    bool k;
-    if (u == f_sink || u == f_diag) {
-      k = true;
-    } else {
+    bool k = true;
+    if (u != f_sink && u != f_diag) {
       const float su = sc[u];
       int rank = 0;
-#pragma unroll 8
-      for (int v = 0; v < n_kv; ++v) {
-        if (v == f_sink || v == f_diag || v == u) continue;
-        const float sv = sc[v];
-        rank += (sv > su || (sv == su && v < u)) ? 1 : 0;
+#pragma unroll 4
+      for (int v = 0; v < n_kv4; v += 4) {
+        const float4 s4 = *reinterpret_cast<const float4*>(&sc[v]);
+        rank += (s4.x > su || (s4.x == su && v < u)) ? 1 : 0;
+        rank += (s4.y > su || (s4.y == su && v + 1 < u)) ? 1 : 0;
+        rank += (s4.z > su || (s4.z == su && v + 2 < u)) ? 1 : 0;
+        rank += (s4.w > su || (s4.w == su && v + 3 < u)) ? 1 : 0;
       }
       k = rank < free_budget;
     }
@@ -187,7 +203,9 @@ hipError_t launch_tile_mask(const Geometry& g, const RopeTab& rt, const void* q,
     a.pooled[i] = i < n_slots ? pooled[i] : nullptr;
     a.delta[i] = i < n_slots ? deltas[i] : 0;
   }
-  hipLaunchKernelGGL(tile_mask_kernel, dim3(g.nt, g.H), dim3(256), 0, stream, a);
+  const int n_kv4 = (n_slots * g.nt + 3) & ~3;
+  const size_t lds = (size_t)n_kv4 * sizeof(float) + (size_t)n_kv4;   // scores, keep flags
+  hipLaunchKernelGGL(tile_mask_kernel, dim3(g.nt, g.H), dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
