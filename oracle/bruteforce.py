@@ -32,11 +32,12 @@ def visible_block(b: int, n: int, n_sink: int, n_window: int) -> bool:
 
 
 def start_times(n: int, w: synth.Workload):
-    """Start time of each visible block b <= n (dict), from the visible layout."""
+    """Start time of each visible block b <= n (dict), from the visible layout: a visible block
+    starts where the visible blocks before it end; relative time puts the visible sinks before 0."""
     vis = [b for b in range(n + 1) if visible_block(b, n, w.n_sink, w.n_window)]
-    n_s = sum(1 for b in vis if b < w.n_sink and b != n)
-    shift = -n_s * w.frames if w.policy == "relative" else 0
-    return {b: w.frames * sum(1 for c in vis if c < b) + shift for b in vis}
+    sink_frames = sum(synth.frames_of(w, b) for b in vis if b < w.n_sink and b != n)
+    shift = -sink_frames if w.policy == "relative" else 0
+    return {b: sum(synth.frames_of(w, c) for c in vis if c < b) + shift for b in vis}
 
 
 def _pair_angles(t, h, wcol, head_dim, theta):
@@ -64,11 +65,13 @@ def _rope_complex(x, t, h, wcol, theta):
 
 def chunk(w: synth.Workload, n: int, s: int, seed: int = 0, contents=None):
     """(O [B, H, d], LSE [H, B]) of query block n at step s, by brute force."""
-    B, H, d = w.shape
-    tok = np.arange(B)
-    f = tok // (w.lat_h * w.lat_w)
-    hh = (tok // w.lat_w) % w.lat_h
-    wc = tok % w.lat_w
+    H, d = w.n_heads, w.head_dim
+
+    def grid(b):
+        tok = np.arange(synth.block_shape(w, b)[0])
+        return tok // (w.lat_h * w.lat_w), (tok // w.lat_w) % w.lat_h, tok % w.lat_w
+
+    B = synth.block_shape(w, n)[0]
     times = start_times(n, w)
     q_st, k_cur, v_cur = synth.qkv(w, n, s, seed)
     ks, vs, key_block = [], [], []
@@ -84,10 +87,12 @@ def chunk(w: synth.Workload, n: int, s: int, seed: int = 0, contents=None):
             else:
                 k_st, v_st = synth.noisy_kv(w, b, seed)
         t0 = times.get(b, 0)
+        f, hh, wc = grid(b)
         ks.append(_rope_complex(synth.as_f64(w, k_st), (t0 + f)[:, None], hh[:, None], wc[:, None],
                                 w.rope_theta))
         vs.append(synth.as_f64(w, v_st))
-        key_block.append(np.full(B, b))
+        key_block.append(np.full(f.size, b))
+    f, hh, wc = grid(n)
     q = _rope_complex(synth.as_f64(w, q_st), (times[n] + f)[:, None], hh[:, None], wc[:, None],
                       w.rope_theta)
     k = np.concatenate(ks, 0)

@@ -77,6 +77,26 @@ def relocation_bases(policy: str, n_sink: int, n_window: int, frames: int):
     raise ValueError(f"unknown relocation policy {policy!r}")
 
 
+def relocation_bases_frames(policy: str, sink_frames, window_frames, current_frames: int):
+    """Start times of the logical slots when blocks have their own frame counts.
+
+    S1: each slot starts where the previous one ends (cumulative frames in logical order, from 0).
+    Relative-time: the window starts at 0 and runs oldest -> newest, the current block follows
+    it, and the sinks sit just before time 0, back to back.  With every block at F frames these
+    are ``relocation_bases`` exactly.
+    """
+    fr = [int(f) for f in sink_frames] + [int(f) for f in window_frames] + [int(current_frames)]
+    starts = [0]
+    for f in fr[:-1]:
+        starts.append(starts[-1] + f)
+    if policy == "s1":
+        return starts
+    if policy == "relative":
+        shift = sum(int(f) for f in sink_frames)
+        return [t - shift for t in starts]
+    raise ValueError(f"unknown relocation policy {policy!r}")
+
+
 def rotate_block(x: np.ndarray, base: int, frames: int, lat_h: int, lat_w: int,
                  theta: float = 10000.0) -> np.ndarray:
     """RoPE of a whole block [B, H, d] whose first frame sits at time `base`."""

@@ -53,9 +53,14 @@ class Stream:
 
     def bases(self, n: int):
         lg = self.logical(n)
-        n_s = sum(1 for r, _ in lg if r == "sink")
-        n_w = sum(1 for r, _ in lg if r == "window")
-        return rope.relocation_bases(self.w.policy, n_s, n_w, self.w.frames)
+        w = self.w
+        if w.frame_pattern is None:
+            n_s = sum(1 for r, _ in lg if r == "sink")
+            n_w = sum(1 for r, _ in lg if r == "window")
+            return rope.relocation_bases(w.policy, n_s, n_w, w.frames)
+        return rope.relocation_bases_frames(
+            w.policy, [synth.frames_of(w, b) for r, b in lg if r == "sink"],
+            [synth.frames_of(w, b) for r, b in lg if r == "window"], synth.frames_of(w, n))
 
     # ---- inputs ------------------------------------------------------------------
     def _kv(self, block: int, kind: str):
@@ -98,7 +103,7 @@ class Stream:
         """
         w = self.w
         heads = list(range(w.n_heads)) if heads is None else list(heads)
-        rows = np.arange(w.block_tokens) if rows is None else np.asarray(rows)
+        rows = np.arange(synth.block_shape(w, n)[0]) if rows is None else np.asarray(rows)
         q, slots = self.slot_inputs(n, s, current)
         bases = self.bases(n)
         job = dict(w=w, q=q, slots=slots, bases=bases, rows=rows, kept=kept)
@@ -114,7 +119,7 @@ class Stream:
 def relocated_head(w: synth.Workload, stored: np.ndarray, head: int, base: int) -> np.ndarray:
     """[B, d] float64 RoPE of one head of a stored block placed at time `base`."""
     x = synth.as_f64(w, stored[:, head, :])
-    f, hh, ww = rope.block_grid(w.frames, w.lat_h, w.lat_w)
+    f, hh, ww = rope.block_grid(stored.shape[0] // (w.lat_h * w.lat_w), w.lat_h, w.lat_w)
     return rope.rotate(x, rope.angles(base + f, hh, ww, w.head_dim, w.rope_theta))
 
 

@@ -21,6 +21,9 @@ Value recipe (the pages give no shapes; the workload descriptions do):
 * TwinCache noisy copies: clean committed K (or V) upcast to fp32, plus
   sigma_b * N(0, 1) with sigma_b ~ U[0.3, 0.8] drawn once per block, then
   rounded to bfloat16.
+* Variable-length blocks: a workload may give a frame pattern; block b then
+  has pattern[b % len(pattern)] latent frames (at most `frames`, the cap) and
+  every tensor of that block is drawn at its own length.
 """
 from __future__ import annotations
 
@@ -32,7 +35,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "TAG_Q", "TAG_K", "TAG_V", "TAG_KN", "TAG_VN",
     "TAG_SIGMA", "rng", "round_bf16", "bf16_to_f32", "draw", "qkv",
-    "committed_kv", "noisy_kv", "as_f64", "tiny",
+    "committed_kv", "noisy_kv", "as_f64", "tiny", "frames_of", "block_shape",
 ]
 
 TAG_Q, TAG_K, TAG_V, TAG_KN, TAG_VN, TAG_SIGMA = 0, 1, 2, 3, 4, 5
@@ -61,6 +64,7 @@ class Workload:
     sigma_range: Tuple[float, float] = (0.3, 0.8)
     rope_theta: float = 10000.0
     tile: int = 128
+    frame_pattern: Optional[Tuple[int, ...]] = None   # frames of block b = pattern[b % len]; None: `frames`
 
     @property
     def block_tokens(self) -> int:
@@ -88,7 +92,26 @@ WORKLOADS: Dict[int, Workload] = {
     5: Workload("c5_540p_blocksparse_bf16", 5, n_heads=24, head_dim=128, frames=3, lat_h=34,
                 lat_w=60, n_sink=1, n_window=3, n_chunks=64, n_steps=4, dtype="bf16",
                 scale=0.5, sparse_keep=0.08),
+    # variable-length blocks (block length follows the control signal, capped): 1-frame blocks
+    # for short controls, 2-3 frames for longer events; relative-time RoPE
+    6: Workload("c6_540p_varlen_bf16", 6, n_heads=24, head_dim=128, frames=3, lat_h=34, lat_w=60,
+                n_sink=1, n_window=3, n_chunks=32, n_steps=4, dtype="bf16", scale=0.5,
+                policy="relative", frame_pattern=(3, 1, 1, 2, 3, 2, 1, 3)),
 }
+
+
+def frames_of(w: Workload, block: int) -> int:
+    """Latent frames of block `block` (the cap `w.frames` unless the workload has a pattern)."""
+    if w.frame_pattern is None:
+        return w.frames
+    f = int(w.frame_pattern[block % len(w.frame_pattern)])
+    if not 1 <= f <= w.frames:
+        raise ValueError(f"frame pattern entry {f} outside [1, {w.frames}]")
+    return f
+
+
+def block_shape(w: Workload, block: int) -> Tuple[int, int, int]:
+    return (frames_of(w, block) * w.lat_h * w.lat_w, w.n_heads, w.head_dim)
 
 
 def tiny(base: int = 1, **kw) -> Workload:
@@ -131,7 +154,7 @@ def as_f32(w: Workload, stored: np.ndarray) -> np.ndarray:
 def draw(w: Workload, chunk: int, step: int, tag: int, seed: int = 0) -> np.ndarray:
     """One [B, H, d] tensor in storage form (uint16 bf16 bits, or float32)."""
     g = rng(seed, w.cfg_id, chunk, step, tag)
-    x = g.standard_normal(size=w.shape, dtype=np.float32) * np.float32(w.scale)
+    x = g.standard_normal(size=block_shape(w, chunk), dtype=np.float32) * np.float32(w.scale)
     return _store(w, x)
 
 
@@ -159,6 +182,6 @@ def noisy_kv(w: Workload, block: int, seed: int = 0, sigma_override: Optional[fl
     out = []
     for stored, tag in ((kc, TAG_KN), (vc, TAG_VN)):
         g = rng(seed, w.cfg_id, block, w.n_steps, tag)
-        n = g.standard_normal(size=w.shape, dtype=np.float32)
+        n = g.standard_normal(size=block_shape(w, block), dtype=np.float32)
         out.append(_store(w, as_f32(w, stored) + s * n))
     return out[0], out[1]
