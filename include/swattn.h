@@ -91,7 +91,7 @@ typedef enum { SW_ROPE_S1_RELOCATE = 0, SW_ROPE_RELATIVE_TIME = 1 } sw_rope_poli
 typedef struct {
   int32_t n_heads;          /* H >= 1 */
   int32_t head_dim;         /* d: 128 (bf16 or fp32) or 64 (fp32) */
-  int32_t frames_per_block; /* F >= 1 */
+  int32_t frames_per_block; /* F >= 1; the cap when blocks carry their own frame count */
   int32_t lat_h, lat_w;     /* latent grid of a frame; B = F*lat_h*lat_w <= 65536 */
   int32_t n_sink;           /* S >= 0 */
   int32_t n_window;         /* W >= 0; S + W + 1 <= 16 */
@@ -115,6 +115,7 @@ typedef struct {
   int32_t physical_slot; /* ring slot holding the block (changes with eviction) */
   int32_t time_base;     /* RoPE time of the block's first frame */
   int32_t twin_complete; /* 1 if the noisy copy exists (always 1 without TwinCache) */
+  int32_t frames;        /* latent frames of the block (<= frames_per_block) */
 } sw_slot_info;
 
 /* Thread-local message of the last failed call ("" if none). */
@@ -143,6 +144,20 @@ sw_status sw_cache_destroy(sw_cache* c);
 sw_status sw_cache_append_block(sw_cache* c, sw_kv_kind kind, const void* k_raw,
                                 const void* v_raw, int64_t block_id);
 
+/* sw_cache_append_block for a block of n_frames latent frames, 1 <= n_frames
+ * <= frames_per_block: K/V are [n_frames*lat_h*lat_w][H][d].  In R2 the length
+ * of a block follows the active control signal up to a cap ("Vidu S2 vs
+ * PixVerse R2" blog, section "Choice 5: how people control it").  The slots
+ * keep their capped size; a block's time base is where the previous slot of
+ * [sinks, window, current] ends (relative time: the window starts at 0, the
+ * sinks sit just before it).  The queries and output of sw_chunk_attend then
+ * have the staged block's length.  Re-appending CURRENT must keep the staged
+ * length; CLEAN with NULL pointers commits the staged length; NOISY must match
+ * the committed block.  SW_ERR_INVALID_ARG for n_frames out of range,
+ * SW_ERR_UNSUPPORTED for a block shorter than the cap in a sparse cache. */
+sw_status sw_cache_append_block_frames(sw_cache* c, sw_kv_kind kind, const void* k_raw,
+                                       const void* v_raw, int64_t block_id, int32_t n_frames);
+
 /* Drop the oldest window block (index remap, no bytes move).  Sinks are never
  * evicted.  SW_ERR_STATE if the window is empty or a NOISY append is due. */
 sw_status sw_cache_evict(sw_cache* c);
@@ -157,7 +172,8 @@ sw_status sw_rope_relocate(sw_cache* c, sw_rope_policy policy);
 sw_status sw_tile_mask_budget(const sw_cache* c, float keep_frac, int32_t* k_row);
 
 /* Build the block-sparse tile mask from the raw queries q_raw [B][H][d] of this
- * step: per head and 128-query tile, score every key tile by the dot product of
+ * step (every cached block at the full frames_per_block length): per head and
+ * 128-query tile, score every key tile by the dot product of
  * mean relocated rotated query and key vectors / sqrt(d), keep key tile 0 of
  * the first sink (if any) and the diagonal current tile, fill up to the budget
  * with the highest scores (ties -> lower index).  Writes ascending linear key
@@ -170,7 +186,8 @@ sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, float keep_frac,
 /* One denoising step's chunk attention for the staged current block:
  *   out[n][h] = softmax_k(<R(p_n) q_n, R(p_k) k> / sqrt(d)) V
  * over keys [sinks, window oldest->newest, current], positions relocated by
- * the current policy.  q_raw [B][H][d] raw (un-rotated) queries; out [B][H][d]
+ * the current policy.  q_raw [B][H][d] raw (un-rotated) queries (B = tokens of
+ * the staged block, see sw_cache_append_block_frames); out [B][H][d]
  * in the cache dtype; lse_out (nullable) [H][B] fp32 natural-log sum of
  * exp(score) per query.  tile_idx == NULL: dense; otherwise block-sparse over
  * the key tiles listed in tile_idx [H][ceil(B/128)][k_row] (as written by

@@ -55,6 +55,7 @@ class Cache:
         self.nbytes = native.sw_cache_required_bytes(self._c)
         self.torch_dtype = _DTYPES[cfg.dtype][1]
         self.shape = (cfg.block_tokens, cfg.n_heads, cfg.head_dim)
+        self.cur_frames = cfg.frames_per_block   # frames of the staged current block
         self.device = device
         if device is None:
             self.pool = None
@@ -92,10 +93,21 @@ class Cache:
         return t.data_ptr()
 
     # ---- the C calls -----------------------------------------------------------
-    def append(self, kind: str, k: Optional[torch.Tensor], v: Optional[torch.Tensor], block_id: int):
-        kp = self._tensor(k, "k") if k is not None else 0
-        vp = self._tensor(v, "v") if v is not None else 0
-        native.sw_cache_append_block(self.handle, KIND[kind], kp, vp, block_id)
+    def shape_of(self, frames: int):
+        return (frames * self.cfg.lat_h * self.cfg.lat_w, self.cfg.n_heads, self.cfg.head_dim)
+
+    def append(self, kind: str, k: Optional[torch.Tensor], v: Optional[torch.Tensor], block_id: int,
+               n_frames: Optional[int] = None):
+        """Append a block (see sw_cache_append_block); n_frames: a block shorter than the cap."""
+        shape = self.shape_of(n_frames) if n_frames is not None else self.shape
+        kp = self._tensor(k, "k", shape=shape) if k is not None else 0
+        vp = self._tensor(v, "v", shape=shape) if v is not None else 0
+        if n_frames is None:
+            native.sw_cache_append_block(self.handle, KIND[kind], kp, vp, block_id)
+        else:
+            native.sw_cache_append_block_frames(self.handle, KIND[kind], kp, vp, block_id, n_frames)
+        if kind == "current":
+            self.cur_frames = self.cfg.frames_per_block if n_frames is None else n_frames
 
     def evict(self):
         native.sw_cache_evict(self.handle)
@@ -118,8 +130,9 @@ class Cache:
 
     def attend(self, q: torch.Tensor, step: str = "final", tile_idx: Optional[torch.Tensor] = None,
                k_row: int = 0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+        shape = self.shape_of(self.cur_frames)
         if out is None:
-            out = torch.empty(self.shape, dtype=self.torch_dtype, device=self.device)
+            out = torch.empty(shape, dtype=self.torch_dtype, device=self.device)
         tp = 0
         if tile_idx is not None:
             if tile_idx.dtype != torch.int32 or not tile_idx.is_cuda or not tile_idx.is_contiguous():
@@ -128,16 +141,18 @@ class Cache:
             if tuple(tile_idx.shape) != (self.cfg.n_heads, nt, k_row):
                 raise ValueError(f"tile_idx shape {tuple(tile_idx.shape)} != {(self.cfg.n_heads, nt, k_row)}")
             tp = tile_idx.data_ptr()
-        lp = self._tensor(lse, "lse", torch.float32, (self.cfg.n_heads, self.cfg.block_tokens)) if lse is not None else 0
-        native.sw_chunk_attend(self.handle, self._tensor(q, "q"), STEP[step], tp, k_row,
-                               self._tensor(out, "out"), lp)
+        lp = self._tensor(lse, "lse", torch.float32, (self.cfg.n_heads, shape[0])) if lse is not None else 0
+        native.sw_chunk_attend(self.handle, self._tensor(q, "q", shape=shape), STEP[step], tp, k_row,
+                               self._tensor(out, "out", shape=shape), lp)
         return out
 
     def inspect(self):
         return native.sw_cache_inspect(self.handle)
 
     def read_slot(self, logical_slot: int, kind: str = "clean"):
-        k = torch.empty(self.shape, dtype=self.torch_dtype, device=self.device)
+        info = self.inspect()
+        frames = info[-1]["frames"] if kind == "current" else info[logical_slot]["frames"]
+        k = torch.empty(self.shape_of(frames), dtype=self.torch_dtype, device=self.device)
         v = torch.empty_like(k)
         native.sw_cache_read_slot(self.handle, logical_slot, KIND[kind], k.data_ptr(), v.data_ptr())
         return k, v

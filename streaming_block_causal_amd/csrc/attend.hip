@@ -110,13 +110,16 @@ __device__ __forceinline__ void load_q(const RopeTab rt, const u16* qp, bool val
 }
 
 // Position i of a workgroup's key schedule -> (slot, 64-key block).  Dense: every block of every
-// slot in logical order.  Sparse: the two halves of each listed 128-key tile.  Returns false for
-// entries to skip (half of a short last tile, or an invalid tile index).
-__device__ __forceinline__ bool block_at(const int32_t* list, int n_slots, int nt, int nkb, int i, int& sl,
-                                         int& kb) {
+// slot in logical order, slot l's blocks at positions [start[l], start[l + 1]) (slots may hold
+// blocks of different lengths).  Sparse: the two halves of each listed 128-key tile.  Returns
+// false for entries to skip (half of a short last tile, or an invalid tile index).
+__device__ __forceinline__ bool block_at(const int32_t* list, const int* start, int n_slots, int nt, int nkb,
+                                         int i, int& sl, int& kb) {
   if (list == nullptr) {
-    sl = i / nkb;
-    kb = i - sl * nkb;
+    int l = 0;
+    while (l + 1 < n_slots && i >= start[l + 1]) ++l;
+    sl = l;
+    kb = i - start[l];
     return true;
   }
   const int tix = list[i >> 1];
@@ -165,6 +168,7 @@ void attend_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) u16 kbuf[NBUF][KB * D];
   __shared__ __attribute__((aligned(1024))) u16 vbuf[NBUF][D * KB];
   __shared__ SlotPtrs sslot[kMaxSlots];
+  __shared__ int sstart[kMaxSlots + 1];   // dense: first schedule position of each slot
 
   // wave index made explicitly uniform: the LDS destinations of the staging loads (M0) then stay
   // in scalar registers
@@ -175,13 +179,22 @@ void attend_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int q = 0; q < kMaxSlots; ++q)
     if (tid == q) sslot[q] = a.slot[q];
+  if (tid == 0) {
+    int t = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxSlots; ++q) {
+      sstart[q] = t;
+      if (q < a.n_slots) t += (a.slot[q].count + KB - 1) / KB;
+    }
+    sstart[kMaxSlots] = t;
+  }
   const RopeTab rt = a.rt;
   const int B = a.B, n_pad = a.n_pad, n_slots = a.n_slots, nt = a.nt;
   const float scale_log2 = a.scale_log2;
   __syncthreads();
 
-  const int nkb = (B + KB - 1) / KB;
-  const int total = SPARSE ? 2 * a.k_row : n_slots * nkb;
+  const int nkb = (B + KB - 1) / KB;   // sparse: every slot holds B keys
+  const int total = SPARSE ? 2 * a.k_row : sstart[n_slots];
   int tile, i0 = 0, i1 = total, piece = -1;
   if ((int)blockIdx.x < a.n_full) {
     tile = xcd_remap(blockIdx.x, a.n_full);
@@ -246,7 +259,7 @@ void attend_bf16_kernel(AttnArgs a) {
   };
 
   // ---- S^T = K Q^T for 64 keys: two 32x32 tiles, lane holds 16 keys of query ln
-  auto qk = [&](const u16* kl, int kb, f32x16& s0, f32x16& s1, const u16* nkb, const u16* nvb, u16* kdst,
+  auto qk = [&](const u16* kl, int kvalid, f32x16& s0, f32x16& s1, const u16* nkb, const u16* nvb, u16* kdst,
                 u16* vdst) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -282,8 +295,7 @@ void attend_bf16_kernel(AttnArgs a) {
       if (jj < NST) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // one staging load
     }
     __builtin_amdgcn_sched_barrier(0);
-    const int kvalid = B - kb * KB;
-    if (kvalid < KB) {
+    if (kvalid < KB) {   // last block of its slot: keys past the block's end do not exist
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -349,7 +361,7 @@ void attend_bf16_kernel(AttnArgs a) {
     int q = i0;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
-      while (q < i1 && !block_at(list, n_slots, nt, nkb, q, bsl[u], bkb[u])) ++q;
+      while (q < i1 && !block_at(list, sstart, n_slots, nt, nkb, q, bsl[u], bkb[u])) ++q;
       pos[u] = q;
       if (q < i1) ++q;
     }
@@ -384,13 +396,13 @@ void attend_bf16_kernel(AttnArgs a) {
       cur_slot = sl;
       load_q<0, kTimeJ>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, qb);
     }
-    qk(kbuf[cb], kb, s0, s1, nk, nv, kbuf[(cb + 1) % NBUF], vbuf[(cb + 1) % NBUF]);
+    qk(kbuf[cb], sslot[sl].count - kb * KB, s0, s1, nk, nv, kbuf[(cb + 1) % NBUF], vbuf[(cb + 1) % NBUF]);
     pend = true;
     pend_buf = cb;
     // look the schedule up one block further while the MFMAs drain
     int q = pos[2] < i1 ? pos[2] + 1 : i1, nsl = 0, nkb2 = 0;
     if (pos[2] < i1) {
-      while (q < i1 && !block_at(list, n_slots, nt, nkb, q, nsl, nkb2)) ++q;
+      while (q < i1 && !block_at(list, sstart, n_slots, nt, nkb, q, nsl, nkb2)) ++q;
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -521,14 +533,15 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
     }
     const float* kbase = static_cast<const float*>(sslot[sl].k) + (size_t)h * a.n_pad * DD;
     const float* vbase = static_cast<const float*>(sslot[sl].v) + (size_t)h * a.n_pad * DD;
-    for (int k0 = 0; k0 < a.B; k0 += KBF) {
+    const int count = sslot[sl].count;
+    for (int k0 = 0; k0 < count; k0 += KBF) {
       __syncthreads();
       for (int i = tid; i < KBF * DD; i += 64) {
         kl[i / DD][i % DD] = kbase[(size_t)k0 * DD + i];
         vl[i / DD][i % DD] = vbase[(size_t)k0 * DD + i];
       }
       __syncthreads();
-      const int nk = min(KBF, a.B - k0);
+      const int nk = min(KBF, count - k0);
       float sc[KBF];
       float mx = -INFINITY;
 #pragma unroll
@@ -594,7 +607,7 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
   a.rt = rt;
   a.part_o = plan.part_o;
   a.part_lse = plan.part_lse;
-  for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0};
+  for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0, 0};
   if (bf16) {
     if (g.d != 128) return hipErrorInvalidValue;
     // tail split: whole rounds of resident workgroups own whole tiles; the tiles of a last,
@@ -623,7 +636,9 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
     constexpr int ROWS = 32 * NW;
     a.n_qt = (g.B + ROWS - 1) / ROWS;
     const int conc = NW == 4 ? 2 * plan.cus : plan.cus;   // workgroups resident at once
-    const int tail = plan_split(a.n_qt * g.H, conc, ROWS, n_slots * ((g.B + KB - 1) / KB));
+    int blocks = 0;
+    for (int l = 0; l < n_slots; ++l) blocks += (slots[l].count + KB - 1) / KB;
+    const int tail = plan_split(a.n_qt * g.H, conc, ROWS, blocks);
     const int split = a.n_split;
     hipLaunchKernelGGL((attend_bf16_kernel<false, NW>), dim3(a.n_full + tail * split), dim3(64 * NW), 0, stream,
                        a);

@@ -54,6 +54,7 @@ namespace swhost {
 struct Entry {
   int64_t block;
   int phys;
+  int frames;   // latent frames of the block (<= the configured cap)
 };
 
 struct Layout {
@@ -149,6 +150,7 @@ struct sw_cache {
   int staging;
   bool staged;
   int64_t staged_id;
+  int staged_frames;
   bool have_commit;
   int64_t last_commit;
   bool noisy_due;
@@ -159,20 +161,38 @@ struct sw_cache {
 
 namespace {
 
-// Time base of each logical slot [sinks, window oldest->newest, current].
-std::vector<int> bases_of(const sw_cache* c) {
-  const int ns = (int)c->sinks.size(), nw = (int)c->window.size(), F = c->L.g.F;
-  std::vector<int> b(ns + nw + 1);
-  for (int l = 0; l < ns + nw + 1; ++l) b[l] = l * F;
-  if (c->policy == SW_ROPE_RELATIVE_TIME)
-    for (int& x : b) x -= ns * F;
-  return b;
-}
-
 std::vector<Entry> history(const sw_cache* c) {
   std::vector<Entry> h(c->sinks.begin(), c->sinks.end());
   h.insert(h.end(), c->window.begin(), c->window.end());
   return h;
+}
+
+// Time base of each logical slot [sinks, window oldest->newest, current]: a slot starts where
+// the previous one ends (l*F when every block has F frames).  Relative time shifts the whole
+// layout so that the window starts at 0 and the sinks sit just before it.
+std::vector<int> bases_of(const sw_cache* c) {
+  const std::vector<Entry> h = history(c);
+  std::vector<int> b(h.size() + 1);
+  int t = 0, sink_frames = 0;
+  for (size_t l = 0; l < h.size(); ++l) {
+    b[l] = t;
+    t += h[l].frames;
+    if (l < c->sinks.size()) sink_frames += h[l].frames;
+  }
+  b[h.size()] = t;
+  if (c->policy == SW_ROPE_RELATIVE_TIME)
+    for (int& x : b) x -= sink_frames;
+  return b;
+}
+
+// tokens of a block of `frames` latent frames
+int tokens_of(const sw_cache* c, int frames) { return frames * c->L.g.lat_h * c->L.g.lat_w; }
+
+// every logical slot (and the staged block) at the full configured length
+bool all_full(const sw_cache* c) {
+  for (const Entry& e : history(c))
+    if (e.frames != c->L.g.F) return false;
+  return !c->staged || c->staged_frames == c->L.g.F;
 }
 
 void fill_tables(const Layout& L, double theta, std::vector<float>& t) {
@@ -197,9 +217,12 @@ sw_status check_ptr(const void* p, const char* name) {
   return SW_OK;
 }
 
-sw_status write_block(sw_cache* c, const void* k, const void* v, char* kd, char* vd, float* pd) {
+sw_status write_block(sw_cache* c, const void* k, const void* v, char* kd, char* vd, float* pd, int frames) {
   if (c->dry) return SW_OK;
-  const hipError_t e = launch_append(c->L.g, c->rt, c->cfg.dtype == SW_BF16, k, v, kd, vd, pd, c->stream);
+  Geometry g = c->L.g;   // the slot keeps its capped stride (n_pad); the block fills its first rows
+  g.B = tokens_of(c, frames);
+  g.nt = (g.B + kTile - 1) / kTile;
+  const hipError_t e = launch_append(g, c->rt, c->cfg.dtype == SW_BF16, k, v, kd, vd, pd, c->stream);
   if (e != hipSuccess) return hip_fail(e, "append kernel launch");
   return SW_OK;
 }
@@ -298,10 +321,11 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
   for (int s = 1; s < L.P; ++s) c->free_slots.push_back(s);
   c->staged = false;
   c->staged_id = -1;
+  c->staged_frames = L.g.F;
   c->have_commit = false;
   c->last_commit = -1;
   c->noisy_due = false;
-  c->noisy_entry = Entry{-1, -1};
+  c->noisy_entry = Entry{-1, -1, 0};
   c->policy = cfg->policy;
   if (dry) c->plan = SplitPlan{0, 0, nullptr, nullptr};
   *out = c;
@@ -317,7 +341,20 @@ sw_status sw_cache_destroy(sw_cache* c) {
 sw_status sw_cache_append_block(sw_cache* c, sw_kv_kind kind, const void* k_raw, const void* v_raw,
                                 int64_t block_id) {
   if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  return sw_cache_append_block_frames(c, kind, k_raw, v_raw, block_id, c->cfg.frames_per_block);
+}
+
+sw_status sw_cache_append_block_frames(sw_cache* c, sw_kv_kind kind, const void* k_raw, const void* v_raw,
+                                       int64_t block_id, int32_t n_frames) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
   if (block_id < 0) return fail(SW_ERR_INVALID_ARG, "block_id must be >= 0");
+  const bool promote_call = kind == SW_KV_CLEAN && k_raw == nullptr && v_raw == nullptr;
+  if (!promote_call) {
+    if (n_frames < 1 || n_frames > c->cfg.frames_per_block)
+      return fail(SW_ERR_INVALID_ARG, "n_frames %d outside [1, %d]", n_frames, c->cfg.frames_per_block);
+    if (c->cfg.sparse && n_frames != c->cfg.frames_per_block)
+      return fail(SW_ERR_UNSUPPORTED, "block-sparse caches hold full-length blocks only");
+  }
   const int S = c->cfg.n_sink, W = c->cfg.n_window;
   switch (kind) {
     case SW_KV_CURRENT: {
@@ -332,11 +369,15 @@ sw_status sw_cache_append_block(sw_cache* c, sw_kv_kind kind, const void* k_raw,
       if (c->have_commit && block_id <= c->last_commit)
         return fail(SW_ERR_STATE, "block %lld is not newer than the last commit %lld", (long long)block_id,
                     (long long)c->last_commit);
+      if (c->staged && n_frames != c->staged_frames)
+        return fail(SW_ERR_STATE, "block %lld is staged with %d frames, not %d", (long long)block_id,
+                    c->staged_frames, n_frames);
       const int s = c->staging;
-      st = write_block(c, k_raw, v_raw, c->kc[s], c->vc[s], c->pc[s]);
+      st = write_block(c, k_raw, v_raw, c->kc[s], c->vc[s], c->pc[s], n_frames);
       if (st != SW_OK) return st;
       c->staged = true;
       c->staged_id = block_id;
+      c->staged_frames = n_frames;
       return SW_OK;
     }
     case SW_KV_CLEAN: {
@@ -368,11 +409,12 @@ sw_status sw_cache_append_block(sw_cache* c, sw_kv_kind kind, const void* k_raw,
         } else {
           if (c->free_slots.empty()) return fail(SW_ERR_STATE, "internal: no free slot");
           phys = c->free_slots.front();
-          const sw_status st = write_block(c, k_raw, v_raw, c->kc[phys], c->vc[phys], c->pc[phys]);
+          const sw_status st = write_block(c, k_raw, v_raw, c->kc[phys], c->vc[phys], c->pc[phys], n_frames);
           if (st != SW_OK) return st;
           c->free_slots.pop_front();
         }
       }
+      const int frames = promote ? c->staged_frames : n_frames;
       if (promote) {
         c->staged = false;
         c->staged_id = -1;
@@ -384,7 +426,7 @@ sw_status sw_cache_append_block(sw_cache* c, sw_kv_kind kind, const void* k_raw,
       c->have_commit = true;
       c->last_commit = block_id;
       if (!dropped) {
-        const Entry e{block_id, phys};
+        const Entry e{block_id, phys, frames};
         if (to_sink) c->sinks.push_back(e);
         else c->window.push_back(e);
         if (c->cfg.twin) {
@@ -403,8 +445,11 @@ sw_status sw_cache_append_block(sw_cache* c, sw_kv_kind kind, const void* k_raw,
       if (block_id != c->noisy_entry.block)
         return fail(SW_ERR_STATE, "noisy copy of block %lld is due, got %lld", (long long)c->noisy_entry.block,
                     (long long)block_id);
+      if (n_frames != c->noisy_entry.frames)
+        return fail(SW_ERR_STATE, "block %lld has %d frames, its noisy copy %d", (long long)block_id,
+                    c->noisy_entry.frames, n_frames);
       const int s = c->noisy_entry.phys;
-      st = write_block(c, k_raw, v_raw, c->kn[s], c->vn[s], c->pn[s]);
+      st = write_block(c, k_raw, v_raw, c->kn[s], c->vn[s], c->pn[s], n_frames);
       if (st != SW_OK) return st;
       c->noisy_due = false;
       return SW_OK;
@@ -453,6 +498,7 @@ sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, float keep_frac, in
   if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache cannot launch kernels");
   if (!c->staged) return fail(SW_ERR_STATE, "no staged current block");
   if (c->noisy_due) return fail(SW_ERR_STATE, "a noisy append is due");
+  if (!all_full(c)) return fail(SW_ERR_UNSUPPORTED, "the tile mask needs full-length blocks");
   int32_t k_row = 0;
   st = sw_tile_mask_budget(c, keep_frac, &k_row);
   if (st != SW_OK) return st;
@@ -487,6 +533,7 @@ sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step, con
   if (tile_idx) {
     if (c->cfg.dtype != SW_BF16) return fail(SW_ERR_UNSUPPORTED, "block-sparse attention needs bf16");
     if (k_row < 1) return fail(SW_ERR_INVALID_ARG, "k_row must be >= 1 with a tile list");
+    if (!all_full(c)) return fail(SW_ERR_UNSUPPORTED, "block-sparse attention needs full-length blocks");
   }
   const std::vector<Entry> hist = history(c);
   const std::vector<int> b = bases_of(c);
@@ -497,11 +544,14 @@ sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step, con
   SlotPtrs slots[kMaxSlots];
   for (int l = 0; l + 1 < n_slots; ++l) {
     const int p = hist[l].phys;
-    slots[l] = SlotPtrs{noisy ? c->kn[p] : c->kc[p], noisy ? c->vn[p] : c->vc[p], b.back() - b[l]};
+    slots[l] = SlotPtrs{noisy ? c->kn[p] : c->kc[p], noisy ? c->vn[p] : c->vc[p], b.back() - b[l],
+                        tokens_of(c, hist[l].frames)};
   }
-  slots[n_slots - 1] = SlotPtrs{c->kc[c->staging], c->vc[c->staging], 0};
-  const hipError_t e = launch_attend(c->L.g, c->rt, c->cfg.dtype == SW_BF16, q_raw, slots, n_slots, tile_idx,
-                                     k_row, out, lse_out, c->plan, c->stream);
+  slots[n_slots - 1] = SlotPtrs{c->kc[c->staging], c->vc[c->staging], 0, tokens_of(c, c->staged_frames)};
+  Geometry gq = c->L.g;   // the queries are the staged block's tokens
+  gq.B = tokens_of(c, c->staged_frames);
+  const hipError_t e = launch_attend(gq, c->rt, c->cfg.dtype == SW_BF16, q_raw, slots, n_slots, tile_idx, k_row,
+                                     out, lse_out, c->plan, c->stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return SW_OK;
 }
@@ -520,11 +570,13 @@ sw_status sw_cache_inspect(const sw_cache* c, sw_slot_info* out, int32_t cap, in
       s.block_id = hist[l].block;
       s.physical_slot = hist[l].phys;
       s.twin_complete = (!c->cfg.twin || !(c->noisy_due && c->noisy_entry.phys == hist[l].phys)) ? 1 : 0;
+      s.frames = hist[l].frames;
     } else {
       s.role = 2;
       s.block_id = c->staged_id;
       s.physical_slot = c->staging;
       s.twin_complete = 1;
+      s.frames = c->staged_frames;
     }
     s.time_base = b[l];
   }
@@ -539,19 +591,23 @@ sw_status sw_cache_read_slot(sw_cache* c, int32_t logical_slot, sw_kv_kind kind,
   if (st != SW_OK) return st;
   if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache holds no data");
   const std::vector<Entry> hist = history(c);
-  int phys;
+  int phys, frames;
   if (kind == SW_KV_CURRENT) {
     if (!c->staged) return fail(SW_ERR_STATE, "no staged current block");
     phys = c->staging;
+    frames = c->staged_frames;
   } else {
     if (logical_slot < 0 || logical_slot >= (int)hist.size())
       return fail(SW_ERR_INVALID_ARG, "logical slot %d out of range [0, %d)", logical_slot, (int)hist.size());
     if (kind == SW_KV_NOISY && !c->cfg.twin) return fail(SW_ERR_STATE, "no noisy copies without TwinCache");
     if (kind != SW_KV_CLEAN && kind != SW_KV_NOISY) return fail(SW_ERR_INVALID_ARG, "unknown kv kind");
     phys = hist[logical_slot].phys;
+    frames = hist[logical_slot].frames;
   }
   const bool noisy = kind == SW_KV_NOISY;
-  hipError_t e = launch_unpack(c->L.g, c->cfg.dtype == SW_BF16, noisy ? c->kn[phys] : c->kc[phys],
+  Geometry g = c->L.g;
+  g.B = tokens_of(c, frames);
+  hipError_t e = launch_unpack(g, c->cfg.dtype == SW_BF16, noisy ? c->kn[phys] : c->kc[phys],
                                noisy ? c->vn[phys] : c->vc[phys], k_out, v_out, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return hip_fail(e, "read-back");

@@ -30,6 +30,7 @@ struct SlotPtrs {
   const void* k;   // rotated K, [H][n_pad][d]
   const void* v;   // bf16: V^T [H][d][n_pad] (keys permuted in groups of 16); fp32: V [H][n_pad][d]
   int delta;       // time base of the current block minus this slot's
+  int count;       // tokens of the slot's block (<= n_pad)
 };
 
 // K1: rotate K at block-local positions, store K and V head-major, pad rows zeroed,
@@ -49,6 +50,8 @@ struct SplitPlan {
 constexpr int kSplitRows = 512 * 128;
 
 // K2 / K3: chunk attention over the given slots (logical order); tile_idx == nullptr -> dense.
+// g.B is the query count (the current block); the keys of slot l are its slots[l].count tokens
+// (block-sparse: every slot holds g.B tokens).
 hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const void* q,
                          const SlotPtrs* slots, int n_slots, const int32_t* tile_idx, int k_row,
                          void* out, float* lse, const SplitPlan& plan, hipStream_t stream);

@@ -38,7 +38,7 @@ class sw_cache_config(ctypes.Structure):
 
 class sw_slot_info(ctypes.Structure):
     _fields_ = [("role", ctypes.c_int32), ("block_id", ctypes.c_int64), ("physical_slot", ctypes.c_int32),
-                ("time_base", ctypes.c_int32), ("twin_complete", ctypes.c_int32)]
+                ("time_base", ctypes.c_int32), ("twin_complete", ctypes.c_int32), ("frames", ctypes.c_int32)]
 
 
 class SwError(RuntimeError):
@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "sw_cache_create": ([ctypes.POINTER(sw_cache_config), P, SZ, P, ctypes.POINTER(H)], ctypes.c_int),
             "sw_cache_destroy": ([H], ctypes.c_int),
             "sw_cache_append_block": ([H, ctypes.c_int, P, P, I64], ctypes.c_int),
+            "sw_cache_append_block_frames": ([H, ctypes.c_int, P, P, I64, I32], ctypes.c_int),
             "sw_cache_evict": ([H], ctypes.c_int),
             "sw_rope_relocate": ([H, ctypes.c_int], ctypes.c_int),
             "sw_tile_mask_budget": ([H, F32, ctypes.POINTER(I32)], ctypes.c_int),
@@ -120,6 +121,12 @@ def sw_cache_append_block(handle: int, kind: int, k_ptr: Optional[int], v_ptr: O
            "sw_cache_append_block")
 
 
+def sw_cache_append_block_frames(handle: int, kind: int, k_ptr: Optional[int], v_ptr: Optional[int],
+                                 block_id: int, n_frames: int):
+    _check(lib().sw_cache_append_block_frames(handle, kind, k_ptr or None, v_ptr or None, block_id, n_frames),
+           "sw_cache_append_block_frames")
+
+
 def sw_cache_evict(handle: int) -> None:
     _check(lib().sw_cache_evict(handle), "sw_cache_evict")
 
@@ -152,7 +159,8 @@ def sw_cache_inspect(handle: int, cap: int = 16):
     n = ctypes.c_int32()
     _check(lib().sw_cache_inspect(handle, arr, cap, ctypes.byref(n)), "sw_cache_inspect")
     return [dict(role=("sink", "window", "current")[s.role], block_id=s.block_id, physical_slot=s.physical_slot,
-                 time_base=s.time_base, twin_complete=bool(s.twin_complete)) for s in arr[:min(cap, n.value)]]
+                 time_base=s.time_base, twin_complete=bool(s.twin_complete), frames=s.frames)
+            for s in arr[:min(cap, n.value)]]
 
 
 def sw_cache_read_slot(handle: int, logical_slot: int, kind: int, k_ptr: int, v_ptr: int) -> None:
