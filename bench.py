@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 PEAK_HBM_GBPS = 8000.0
 
-WORKLOADS = {"c2": 2, "c3": 3, "c4": 4, "c5": 5}
+WORKLOADS = {"c2": 2, "c3": 3, "c4": 4, "c5": 5, "c6": 6}
 
 
 def attn_flops(B, H, d, n_keys):
@@ -130,44 +130,67 @@ def main():
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
 
-    def draw():
-        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * w.scale).to(torch.bfloat16)
+    varlen = w.frame_pattern is not None
+    hw = w.lat_h * w.lat_w
+    frame_counts = sorted(set(w.frame_pattern)) if varlen else [w.frames]
 
-    # two input sets (alternating chunks), resident in HBM before timing
-    sets = [[(draw(), draw(), draw()) for _ in range(T)] for _ in range(2)]
-    noisy = [(draw(), draw()) for _ in range(2)]
-    out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    def draw(frames):
+        return (torch.randn((frames * hw, H, d), generator=gen, device=dev, dtype=torch.float32)
+                * w.scale).to(torch.bfloat16)
+
+    # two input sets per block length (alternating chunks), resident in HBM before timing
+    sets = {f: [[(draw(f), draw(f), draw(f)) for _ in range(T)] for _ in range(2)] for f in frame_counts}
+    noisy = {f: [(draw(f), draw(f)) for _ in range(2)] for f in frame_counts}
+    outs = {f: torch.empty((f * hw, H, d), dtype=torch.bfloat16, device=dev) for f in frame_counts}
     nt = -(-B // 128)
+
+    def frames_of(b):
+        return synth.frames_of(w, b)
+
+    def append_current(k, v, b):
+        cache.append("current", k, v, b, n_frames=frames_of(b) if varlen else None)
 
     n_slots_full = w.n_sink + w.n_window + 1
     state = {"block": 0, "window": 0, "sinks": 0}
+    history = []            # frames of the committed blocks the cache holds, logical order
 
     def commit():
         b = state["block"]
         if state["sinks"] >= w.n_sink and w.n_window > 0 and state["window"] == w.n_window:
             cache.evict()
             state["window"] -= 1
+            history.pop(state["sinks"])
         cache.append("clean", None, None, b)
         if state["sinks"] < w.n_sink:
             state["sinks"] += 1
-        else:
+            history.append(frames_of(b))
+        elif w.n_window > 0:
             state["window"] += 1
+            history.append(frames_of(b))
         if w.twin:
-            kn, vn = noisy[b % 2]
-            cache.append("noisy", kn, vn, b)
+            kn, vn = noisy[frames_of(b)][b % 2]
+            cache.append("noisy", kn, vn, b, n_frames=frames_of(b) if varlen else None)
         state["block"] += 1
 
     ev = {"attn": [], "append": [], "mask": []}
     last_mask = {}
 
+    flops_timed = {"sum": 0.0, "frames": 0}
+
     def chunk(record):
         b = state["block"]
+        fb = frames_of(b)
+        out = outs[fb]
+        if record:
+            keys = (sum(history) + fb) * hw
+            flops_timed["sum"] += T * attn_flops(fb * hw, H, d, keys)
+            flops_timed["frames"] += fb
         for s in range(T):
-            q, k, v = sets[b % 2][s]
+            q, k, v = sets[fb][b % 2][s]
             if record:
                 e0, e1, em, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
                 e0.record(stream)
-            cache.append("current", k, v, b)
+            append_current(k, v, b)
             if record:
                 e1.record(stream)
             step = "final" if s == T - 1 else "intermediate"
@@ -191,8 +214,8 @@ def main():
     # fill the cache to steady state (appends and commits only, so every attention launch
     # below -- and in a profiler trace of this script -- has the full key set), then warm up
     while state["block"] < n_slots_full - 1:
-        q, k, v = sets[state["block"] % 2][T - 1]
-        cache.append("current", k, v, state["block"])
+        q, k, v = sets[frames_of(state["block"])][state["block"] % 2][T - 1]
+        append_current(k, v, state["block"])
         commit()
     for _ in range(args.warmup):
         chunk(False)
@@ -224,7 +247,9 @@ def main():
     mask_ms = [a.elapsed_time(b) for a, b in ev["mask"]]
     app_ms = [a.elapsed_time(b) for a, b in ev["append"]]
     keys = n_slots_full * B
-    if w.sparse_keep is None:
+    if varlen:
+        flops_call = flops_timed["sum"] / (T * args.steps)   # mean over the timed calls
+    elif w.sparse_keep is None:
         flops_call = attn_flops(B, H, d, keys)
     else:
         # exact kept-tile work of the last mask: sum of valid_q * valid_k over kept tile pairs
@@ -232,7 +257,7 @@ def main():
         valid = torch.clamp(B - 128 * torch.arange(nt, device=dev), max=128).double()
         vk = valid[idx % nt]                                   # [H, nt, k_row]
         flops_call = float(4.0 * d * (vk.sum(dim=2) * valid[None, :]).sum().item())
-    flops_chunk = flops_call * T
+    flops_chunk = flops_timed["sum"] / args.steps if varlen else flops_call * T
     ms_chunk = dt / args.steps * 1e3
     avg_attn = sum(attn_ms) / len(attn_ms)
     avg_mask = sum(mask_ms) / len(mask_ms)
@@ -256,8 +281,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "block_tokens": B, "keys": keys, "heads": H, "head_dim": d,
                    "n_sink": w.n_sink, "n_window": w.n_window, "steps_per_chunk": T,
-                   "latent_grid": [w.frames, w.lat_h, w.lat_w], "parallelism": "single GPU"},
-        "latent_frames_per_s": w.frames / (ms_chunk * 1e-3),
+                   "latent_grid": [w.frames, w.lat_h, w.lat_w],
+                   "frame_pattern": list(w.frame_pattern) if w.frame_pattern else None,
+                   "parallelism": "single GPU"},
+        "latent_frames_per_s": (flops_timed["frames"] / args.steps if varlen else w.frames) / (ms_chunk * 1e-3),
         "frac_of_bf16_peak_step": flops_chunk / (ms_chunk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "attention_ms_per_call": avg_attn,
         "attention_ms_p50_p95": [p50, p95],

@@ -109,23 +109,16 @@ __device__ __forceinline__ void load_q(const RopeTab rt, const u16* qp, bool val
   }
 }
 
-// Position i of a workgroup's key schedule -> (slot, 64-key block).  Dense: every block of every
-// slot in logical order, slot l's blocks at positions [start[l], start[l + 1]) (slots may hold
-// blocks of different lengths).  Sparse: the two halves of each listed 128-key tile.  Returns
-// false for entries to skip (half of a short last tile, or an invalid tile index).
-__device__ __forceinline__ bool block_at(const int32_t* list, const int* start, int n_slots, int nt, int nkb,
-                                         int i, int& sl, int& kb) {
-  if (list == nullptr) {
-    int l = 0;
-    while (l + 1 < n_slots && i >= start[l + 1]) ++l;
-    sl = l;
-    kb = i - start[l];
-    return true;
-  }
+// Sparse schedule: position i -> (slot, 64-key block, keys in the block) from the two halves of
+// each listed 128-key tile (every slot holds B keys).  Returns false for entries to skip (half of
+// a short last tile, or an invalid tile index).
+__device__ __forceinline__ bool block_at(const int32_t* list, int B, int n_slots, int nt, int nkb, int i, int& sl,
+                                         int& kb, int& kvalid) {
   const int tix = list[i >> 1];
   if (tix < 0 || tix >= n_slots * nt) return false;   // never read outside the cache
   sl = tix / nt;
   kb = 2 * (tix - sl * nt) + (i & 1);
+  kvalid = B - kb * KB;
   return kb < nkb;
 }
 
@@ -168,7 +161,6 @@ void attend_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) u16 kbuf[NBUF][KB * D];
   __shared__ __attribute__((aligned(1024))) u16 vbuf[NBUF][D * KB];
   __shared__ SlotPtrs sslot[kMaxSlots];
-  __shared__ int sstart[kMaxSlots + 1];   // dense: first schedule position of each slot
 
   // wave index made explicitly uniform: the LDS destinations of the staging loads (M0) then stay
   // in scalar registers
@@ -179,22 +171,19 @@ void attend_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int q = 0; q < kMaxSlots; ++q)
     if (tid == q) sslot[q] = a.slot[q];
-  if (tid == 0) {
-    int t = 0;
+  // dense schedule: every 64-key block of every slot in logical order (slots may hold blocks of
+  // different lengths)
+  int dense_total = 0;
 #pragma unroll
-    for (int q = 0; q < kMaxSlots; ++q) {
-      sstart[q] = t;
-      if (q < a.n_slots) t += (a.slot[q].count + KB - 1) / KB;
-    }
-    sstart[kMaxSlots] = t;
-  }
+  for (int q = 0; q < kMaxSlots; ++q)
+    if (q < a.n_slots) dense_total += (a.slot[q].count + KB - 1) / KB;
   const RopeTab rt = a.rt;
   const int B = a.B, n_pad = a.n_pad, n_slots = a.n_slots, nt = a.nt;
   const float scale_log2 = a.scale_log2;
   __syncthreads();
 
   const int nkb = (B + KB - 1) / KB;   // sparse: every slot holds B keys
-  const int total = SPARSE ? 2 * a.k_row : sstart[n_slots];
+  const int total = SPARSE ? 2 * a.k_row : dense_total;
   int tile, i0 = 0, i1 = total, piece = -1;
   if ((int)blockIdx.x < a.n_full) {
     tile = xcd_remap(blockIdx.x, a.n_full);
@@ -356,12 +345,43 @@ void attend_bf16_kernel(AttnArgs a) {
   f32x16 s0, s1;
 
   // schedule positions: p[0] computed, p[1] staged, p[2] looked up ahead
-  int pos[3], bsl[3], bkb[3];
+  // Dense: positions are looked up once each, in increasing order, so a cursor walks the slots;
+  // a slot's key count is read (from LDS, made scalar) only when the cursor enters the slot, and
+  // schedule, slot and key count stay in scalar registers.
+  int csl = 0, ckb = 0, ccnt = 0, cnb = 0;
+  auto enter = [&](int l) {
+    csl = l;
+    ckb = 0;
+    ccnt = __builtin_amdgcn_readfirstlane(sslot[l].count);
+    cnb = (ccnt + KB - 1) / KB;
+  };
+  if (!SPARSE) {
+    enter(0);
+    int rem = i0;
+    while (rem >= cnb && csl + 1 < n_slots) {
+      rem -= cnb;
+      enter(csl + 1);
+    }
+    ckb = rem;
+  }
+  // the schedule entry at or after position q (q is left on it): slot, block, keys in the block
+  auto lookup = [&](int& q, int& sl, int& kb, int& kv) {
+    if (SPARSE) {
+      while (q < i1 && !block_at(list, B, n_slots, nt, nkb, q, sl, kb, kv)) ++q;
+    } else if (q < i1) {
+      while (ckb >= cnb && csl + 1 < n_slots) enter(csl + 1);   // (skips empty slots)
+      sl = csl;
+      kb = ckb;
+      kv = ccnt - ckb * KB;
+      ++ckb;
+    }
+  };
+  int pos[3], bsl[3], bkb[3], bkv[3];
   {
     int q = i0;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
-      while (q < i1 && !block_at(list, sstart, n_slots, nt, nkb, q, bsl[u], bkb[u])) ++q;
+      lookup(q, bsl[u], bkb[u], bkv[u]);
       pos[u] = q;
       if (q < i1) ++q;
     }
@@ -380,7 +400,7 @@ void attend_bf16_kernel(AttnArgs a) {
   // one pipeline step: softmax and P.V of block n - 1, the barrier of block n, then S of block n
   // from buffer cb while block n + 1 is requested into the next buffer
   auto step = [&](const int cb) {
-    const int sl = bsl[0], kb = bkb[0];
+    const int sl = bsl[0], kvalid = bkv[0];
     auto sync = [&]() {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of block n has landed
       // ... and everyone's has; the buffer block n + 1 goes to (that of block n + 1 - NBUF) is
@@ -396,23 +416,25 @@ void attend_bf16_kernel(AttnArgs a) {
       cur_slot = sl;
       load_q<0, kTimeJ>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, qb);
     }
-    qk(kbuf[cb], sslot[sl].count - kb * KB, s0, s1, nk, nv, kbuf[(cb + 1) % NBUF], vbuf[(cb + 1) % NBUF]);
+    qk(kbuf[cb], kvalid, s0, s1, nk, nv, kbuf[(cb + 1) % NBUF], vbuf[(cb + 1) % NBUF]);
     pend = true;
     pend_buf = cb;
     // look the schedule up one block further while the MFMAs drain
-    int q = pos[2] < i1 ? pos[2] + 1 : i1, nsl = 0, nkb2 = 0;
+    int q = pos[2] < i1 ? pos[2] + 1 : i1, nsl = 0, nkb2 = 0, nkv = 0;
     if (pos[2] < i1) {
-      while (q < i1 && !block_at(list, sstart, n_slots, nt, nkb, q, nsl, nkb2)) ++q;
+      lookup(q, nsl, nkb2, nkv);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       pos[u] = pos[u + 1];
       bsl[u] = bsl[u + 1];
       bkb[u] = bkb[u + 1];
+      bkv[u] = bkv[u + 1];
     }
     pos[2] = q;
     bsl[2] = nsl;
     bkb[2] = nkb2;
+    bkv[2] = nkv;
     block_base(pos[1] < i1, bsl[1], bkb[1], nk, nv);
   };
   while (pos[0] < i1) {
@@ -612,13 +634,29 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
     if (g.d != 128) return hipErrorInvalidValue;
     // tail split: whole rounds of resident workgroups own whole tiles; the tiles of a last,
     // partial round are cut into up to kMaxSplit key ranges (only when a whole round exists)
+    // fewer tiles than resident workgroups (short blocks): every tile is cut so that the pieces
+    // fill whole rounds (the smallest cut reaching 95% of the slots, if it gains 5 points)
     auto plan_split = [&](int tiles, int conc, int rows, int blocks) {
       const int tail = conc > 0 ? tiles % conc : 0;
+      const int max_pieces = plan.part_o ? plan.max_rows / rows : 0;
       int split = 0;
-      if (plan.part_o && conc > 0 && tiles >= conc && tail > 0) {
-        split = std::min(std::min(kMaxSplit, conc / tail), (plan.max_rows / rows) / tail);
-        split = std::min(split, blocks);   // no empty key ranges
-        if (split < 2) split = 0;
+      if (plan.part_o && conc > 0 && tail > 0) {
+        if (tiles >= conc) {
+          split = std::min(std::min(kMaxSplit, conc / tail), max_pieces / tail);
+          split = std::min(split, blocks);   // no empty key ranges
+          if (split < 2) split = 0;
+        } else {
+          double best = (double)tiles / conc;
+          for (int sp = 2; sp <= std::min(kMaxSplit, blocks) && tiles * sp <= max_pieces; ++sp) {
+            const int pieces = tiles * sp, rounds = (pieces + conc - 1) / conc;
+            const double util = (double)pieces / ((double)rounds * conc);
+            if (util > best + 0.05) {
+              best = util;
+              split = sp;
+              if (util >= 0.95) break;
+            }
+          }
+        }
       }
       a.n_full = split ? tiles - tail : tiles;
       a.n_split = split;

@@ -47,7 +47,7 @@ struct SplitPlan {
   float* part_o;     // [max_rows][d]
   float* part_lse;   // [max_rows]
 };
-constexpr int kSplitRows = 512 * 128;
+constexpr int kSplitRows = 1024 * 256;   // 1024 pieces of a 256-query tile
 
 // K2 / K3: chunk attention over the given slots (logical order); tile_idx == nullptr -> dense.
 // g.B is the query count (the current block); the keys of slot l are its slots[l].count tokens

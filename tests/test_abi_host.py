@@ -30,7 +30,7 @@ def test_required_bytes_closed_form():
     n = native.sw_cache_required_bytes(c)
     slot = 24 * 6144 * 128 * 2                       # one K (or V) slot, head-major, padded to 6144
     table = 2 * (15 * 22 + 34 * 21 + 60 * 21) * 4     # fp32 cos/sin for t, h, w
-    work = 512 * 128 * 128 * 4 + 512 * 128 * 4       # partial results of split attention tiles
+    work = 1024 * 256 * 128 * 4 + 1024 * 256 * 4     # partial results of split attention tiles
     assert n == 5 * 2 * slot + ((table + 255) // 256) * 256 + work
     tw = config_for(synth.WORKLOADS[3]).to_c()
     assert native.sw_cache_required_bytes(tw) == 5 * 4 * slot + ((table + 255) // 256) * 256 + work

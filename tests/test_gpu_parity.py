@@ -264,14 +264,40 @@ def test_sparse_mid_all_rows_and_keep_all():
         out = c.attend(to_dev(w, q), "final", tile_idx=tiles, k_row=tiles.shape[2], lse=lse)
         torch.cuda.synchronize()
         _check(w, to_f64(out), to_f64(lse), ref, rl, f"chunk {n}")
-        # keep-all tile list == dense call, exactly (same tile order)
+        # keep-all tile list against the dense call.  At this small shape the dense launch cuts
+        # its few query tiles into key ranges merged afterwards and the sparse one does not: the
+        # probabilities are rounded to bf16 against another running maximum, so the two agree
+        # to that rounding, not bit for bit (the bitwise case is the test below).
         nt = otm.n_tiles(w.block_tokens)
         L = len(st.logical(n))
         full = torch.arange(L * nt, dtype=torch.int32, device="cuda").repeat(w.n_heads, nt, 1).contiguous()
         o_all = c.attend(to_dev(w, q), "final", tile_idx=full, k_row=L * nt)
         o_dense = c.attend(to_dev(w, q), "final")
         torch.cuda.synchronize()
-        assert torch.equal(o_all, o_dense)
+        diff = float((o_all.float() - o_dense.float()).abs().max())
+        assert diff <= 2e-3, (n, diff)
+        commit_block(c, w, n, n)
+
+
+def test_sparse_keep_all_equals_dense_bitwise():
+    """With as many query tiles as compute units the dense launch is not split, and the sparse
+    kernel given every key tile in ascending order does the dense kernel's arithmetic exactly."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_qt = 4                                                          # B = 960 -> 4 tiles of 256 rows
+    w = synth.tiny(5, n_heads=cus // n_qt, lat_h=16, lat_w=20, n_chunks=4, n_steps=1, sparse_keep=0.3)
+    _say(f"[sparse keep-all bitwise] H={w.n_heads}")
+    c = _cache(w)
+    st = ostream.Stream(w)
+    nt = otm.n_tiles(w.block_tokens)
+    for n in range(w.n_chunks):
+        q, k, v = synth.qkv(w, n, 1)
+        c.append("current", to_dev(w, k), to_dev(w, v), n)
+        L = len(st.logical(n))
+        full = torch.arange(L * nt, dtype=torch.int32, device="cuda").repeat(w.n_heads, nt, 1).contiguous()
+        o_all = c.attend(to_dev(w, q), "final", tile_idx=full, k_row=L * nt)
+        o_dense = c.attend(to_dev(w, q), "final")
+        torch.cuda.synchronize()
+        assert torch.equal(o_all, o_dense), n
         commit_block(c, w, n, n)
 
 
