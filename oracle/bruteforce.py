@@ -10,7 +10,10 @@ an explicit boolean mask.  Meant for tiny workloads only.
 Sources: "Vidu S2 vs PixVerse R2" blog (orkas.ai), sections "What real-time
 changes" (each block sees only earlier blocks) and "Choice 3: bounded memory"
 (permanent first blocks, a window of recent blocks, positions kept inside the
-trained range).
+trained range).  Editing streams (Vidu S2 paper read, section 2.6): every source
+frame that has arrived is laid out too, and a source frame is visible to a query
+exactly when both belong to the same instant of the stream (the same global
+frame index), never across instants.
 """
 from __future__ import annotations
 
@@ -38,6 +41,11 @@ def start_times(n: int, w: synth.Workload):
     sink_frames = sum(synth.frames_of(w, b) for b in vis if b < w.n_sink and b != n)
     shift = -sink_frames if w.policy == "relative" else 0
     return {b: sum(synth.frames_of(w, c) for c in vis if c < b) + shift for b in vis}
+
+
+def instant(w: synth.Workload, b: int, f):
+    """Global frame index (instant of the stream) of frame f of block b."""
+    return sum(synth.frames_of(w, c) for c in range(b)) + f
 
 
 def _pair_angles(t, h, wcol, head_dim, theta):
@@ -99,7 +107,24 @@ def chunk(w: synth.Workload, n: int, s: int, seed: int = 0, contents=None):
     v = np.concatenate(vs, 0)
     kb = np.concatenate(key_block)
     allowed = np.array([visible_block(int(b), n, w.n_sink, w.n_window) for b in kb])
-    mask = torch.from_numpy(np.broadcast_to(allowed, (B, kb.size)).copy())
+    mask = np.broadcast_to(allowed, (B, kb.size))
+    if w.editing and n >= 1:
+        # source frames of every block that has arrived, at their target block's positions
+        sk, sv, s_inst = [], [], []
+        for b in range(1, n + 1):
+            k_src, v_src = synth.source_kv(w, b, seed) if contents is None else contents(b, "source")
+            t0 = times.get(b, 0)
+            fb, hb, wb = grid(b)
+            sk.append(_rope_complex(synth.as_f64(w, k_src), (t0 + fb)[:, None], hb[:, None], wb[:, None],
+                                    w.rope_theta))
+            sv.append(synth.as_f64(w, v_src))
+            s_inst.append(instant(w, b, fb))
+        s_inst = np.concatenate(s_inst)
+        q_inst = instant(w, n, f)
+        k = np.concatenate([k] + sk, 0)
+        v = np.concatenate([v] + sv, 0)
+        mask = np.concatenate([mask, q_inst[:, None] == s_inst[None, :]], axis=1)
+    mask = torch.from_numpy(np.ascontiguousarray(mask))
     qt = torch.from_numpy(q).permute(1, 0, 2)          # [H, B, d]
     kt = torch.from_numpy(k).permute(1, 0, 2)
     vt = torch.from_numpy(v).permute(1, 0, 2)

@@ -8,6 +8,15 @@ over the materialised keys [sink blocks, window blocks oldest->newest, current
 block], positions p = (t, h, w) relocated as in ``rope.relocation_bases``, and
 M = -inf only on key tiles the block-sparse mask drops.
 
+Editing streams (frame-aligned attention: Vidu S2 paper read, section 2.6 on
+the editing model; the BloomBook Vidu S2 tutorial, section "S2-Editing" and the
+figure caption on the input structure; "Vidu S2 vs PixVerse R2" blog, section
+"Choice 5: how people control it"): block 0 holds the reference image and stays
+as a sink, seen by every frame; chunk n >= 1 also sees the source-video frames
+that arrive with it, a query of frame f only the source frame of the same
+instant f, at the same (t, h, w) positions as the target frame.  Source frames
+are consumed with their chunk and never enter the history.
+
 Sources: "Vidu S2 vs PixVerse R2" blog (orkas.ai), sections "What real-time
 changes" (blocks in time order, each sees only the past), "Choice 3: bounded
 memory" (sinks + sliding window, RoPE relocation / relative-time RoPE,
@@ -34,7 +43,8 @@ class Stream:
     """Walks a workload's cache model and computes any (chunk, step) call in fp64.
 
     `contents(block_id, kind)` may replace the stored K/V of a history block
-    ('clean' or 'noisy'); by default blocks are the seeded draws.
+    ('clean' or 'noisy') or a chunk's source frames ('source'); where it returns None
+    (or is not given) blocks are the seeded draws.
     """
 
     def __init__(self, w: synth.Workload, seed: int = 0,
@@ -54,7 +64,7 @@ class Stream:
     def bases(self, n: int):
         lg = self.logical(n)
         w = self.w
-        if w.frame_pattern is None:
+        if w.frame_pattern is None and not w.editing:
             n_s = sum(1 for r, _ in lg if r == "sink")
             n_w = sum(1 for r, _ in lg if r == "window")
             return rope.relocation_bases(w.policy, n_s, n_w, w.frames)
@@ -66,11 +76,10 @@ class Stream:
     def _kv(self, block: int, kind: str):
         key = (block, kind)
         if key not in self._memo:
-            if self.contents is not None:
-                kv = self.contents(block, kind)
-            elif kind == "clean":
+            kv = self.contents(block, kind) if self.contents is not None else None
+            if kv is None and kind == "clean":
                 kv = synth.committed_kv(self.w, block, self.seed)
-            else:
+            elif kv is None:
                 kv = synth.noisy_kv(self.w, block, self.seed, self.sigma_override)
             self._memo[key] = kv
         return self._memo[key]
@@ -90,7 +99,18 @@ class Stream:
                 kind = "noisy" if (w.twin and s < w.n_steps) else "clean"
                 k, v = self._kv(b, kind)
                 out.append((role, b, k, v))
+        if w.editing and n >= 1:
+            ks, vs = self.source(n)
+            out.append(("source", n, ks, vs))
         return q, out
+
+    def source(self, n: int):
+        """Source-frame K/V of chunk n (replaceable through `contents(n, 'source')`)."""
+        if self.contents is not None:
+            kv = self.contents(n, "source")
+            if kv is not None:
+                return kv
+        return synth.source_kv(self.w, n, self.seed)
 
     # ---- the call ----------------------------------------------------------------
     def call(self, n: int, s: int, heads: Optional[Sequence[int]] = None,
@@ -106,6 +126,8 @@ class Stream:
         rows = np.arange(synth.block_shape(w, n)[0]) if rows is None else np.asarray(rows)
         q, slots = self.slot_inputs(n, s, current)
         bases = self.bases(n)
+        if slots[-1][0] == "source":
+            bases = bases + [bases[-1]]   # source frames sit at the current block's positions
         job = dict(w=w, q=q, slots=slots, bases=bases, rows=rows, kept=kept)
         if workers > 1 and len(heads) > 1:
             res = _pool_map(job, heads, workers)
@@ -131,7 +153,11 @@ def _one_head(job, h):
     k_all = np.concatenate(k_rel, axis=0)
     kept = None
     vis = None
-    if job["kept"] is not None:
+    if slots[-1][0] == "source":
+        if job["kept"] is not None or w.sparse_keep is not None:
+            raise ValueError("frame-aligned editing attention is dense only")
+        vis = _frame_aligned(w, rows, [k.shape[0] for (_, _, k, _) in slots])
+    elif job["kept"] is not None:
         kept = job["kept"][h]
     elif w.sparse_keep is not None:
         kept, _, _ = tilemask.build(q_rel, k_rel, [r for r, _, _, _ in slots], w.sparse_keep, w.tile)
@@ -139,6 +165,18 @@ def _one_head(job, h):
         vis = tilemask.visible(kept, w.block_tokens, len(slots), w.tile)[rows]
     o, lse = attention.attend(q_rel[rows], k_all, v_all, vis)
     return o, lse, kept
+
+
+def _frame_aligned(w: synth.Workload, rows, lengths):
+    """Visibility [rows, keys] with the source block last: every history and current key is
+    visible, a source key only to the queries of its own frame."""
+    hw = w.lat_h * w.lat_w
+    rows = np.asarray(rows)
+    n_other = sum(lengths[:-1])
+    src_frame = np.arange(lengths[-1]) // hw
+    vis = np.ones((rows.size, n_other + lengths[-1]), dtype=bool)
+    vis[:, n_other:] = (rows // hw)[:, None] == src_frame[None, :]
+    return vis
 
 
 _JOB = None

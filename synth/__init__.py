@@ -1,6 +1,6 @@
 """Seeded synthetic inputs for streaming block-causal chunk attention.
 
-This module describes the five synthetic workloads (shapes, cache sizes,
+This module describes the synthetic workloads (shapes, cache sizes,
 stream lengths, value distributions) and draws their Q/K/V tensors from a
 seed.  It computes no step of the attention method: it only draws numbers and
 rounds fp32 draws to bfloat16 bit patterns, so that the fp64 oracle and the
@@ -24,6 +24,9 @@ Value recipe (the pages give no shapes; the workload descriptions do):
 * Variable-length blocks: a workload may give a frame pattern; block b then
   has pattern[b % len(pattern)] latent frames (at most `frames`, the cap) and
   every tensor of that block is drawn at its own length.
+* Editing streams: block 0 holds the reference-image latents (`ref_frames`
+  frames) and every later block b comes with the K/V of its source-video frames,
+  drawn like a block's K/V at block b's shape, independent of the step.
 """
 from __future__ import annotations
 
@@ -35,10 +38,10 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "TAG_Q", "TAG_K", "TAG_V", "TAG_KN", "TAG_VN",
     "TAG_SIGMA", "rng", "round_bf16", "bf16_to_f32", "draw", "qkv",
-    "committed_kv", "noisy_kv", "as_f64", "tiny", "frames_of", "block_shape",
+    "committed_kv", "noisy_kv", "source_kv", "as_f64", "tiny", "frames_of", "block_shape",
 ]
 
-TAG_Q, TAG_K, TAG_V, TAG_KN, TAG_VN, TAG_SIGMA = 0, 1, 2, 3, 4, 5
+TAG_Q, TAG_K, TAG_V, TAG_KN, TAG_VN, TAG_SIGMA, TAG_KS, TAG_VS = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -65,6 +68,8 @@ class Workload:
     rope_theta: float = 10000.0
     tile: int = 128
     frame_pattern: Optional[Tuple[int, ...]] = None   # frames of block b = pattern[b % len]; None: `frames`
+    editing: bool = False            # block 0 is the reference, blocks >= 1 carry source frames
+    ref_frames: Optional[int] = None  # editing: latent frames of the reference block (None: as block 0)
 
     @property
     def block_tokens(self) -> int:
@@ -97,14 +102,23 @@ WORKLOADS: Dict[int, Workload] = {
     6: Workload("c6_540p_varlen_bf16", 6, n_heads=24, head_dim=128, frames=3, lat_h=34, lat_w=60,
                 n_sink=1, n_window=3, n_chunks=32, n_steps=4, dtype="bf16", scale=0.5,
                 policy="relative", frame_pattern=(3, 1, 1, 2, 3, 2, 1, 3)),
+    # streaming video editing: a one-frame reference image pinned as the sink, a window of edited
+    # (target) blocks, and per chunk the source-video frames of the same instants
+    7: Workload("c7_540p_editing_bf16", 7, n_heads=24, head_dim=128, frames=3, lat_h=34, lat_w=60,
+                n_sink=1, n_window=3, n_chunks=32, n_steps=4, dtype="bf16", scale=0.5,
+                editing=True, ref_frames=1),
 }
 
 
 def frames_of(w: Workload, block: int) -> int:
-    """Latent frames of block `block` (the cap `w.frames` unless the workload has a pattern)."""
-    if w.frame_pattern is None:
+    """Latent frames of block `block` (the cap `w.frames` unless the workload has a pattern, or the
+    block is an editing stream's reference)."""
+    if w.editing and block == 0 and w.ref_frames is not None:
+        f = int(w.ref_frames)
+    elif w.frame_pattern is None:
         return w.frames
-    f = int(w.frame_pattern[block % len(w.frame_pattern)])
+    else:
+        f = int(w.frame_pattern[block % len(w.frame_pattern)])
     if not 1 <= f <= w.frames:
         raise ValueError(f"frame pattern entry {f} outside [1, {w.frames}]")
     return f
@@ -173,6 +187,13 @@ def sigma(w: Workload, block: int, seed: int = 0) -> float:
     g = rng(seed, w.cfg_id, block, 0, TAG_SIGMA)
     lo, hi = w.sigma_range
     return float(g.uniform(lo, hi))
+
+
+def source_kv(w: Workload, block: int, seed: int = 0):
+    """K/V of the source-video frames that come with block `block` (>= 1) of an editing stream."""
+    if not w.editing or block < 1:
+        raise ValueError("source frames exist for blocks >= 1 of an editing workload")
+    return draw(w, block, 0, TAG_KS, seed), draw(w, block, 0, TAG_VS, seed)
 
 
 def noisy_kv(w: Workload, block: int, seed: int = 0, sigma_override: Optional[float] = None):
