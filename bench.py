@@ -1,13 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark of streaming block-causal chunk attention on one MI355X.
 
-A step is one chunk of the 540p dense stream in steady state (full window,
+A step is one chunk of a 540p (or 720p) stream in steady state (full window,
 eviction every chunk): for each of the 4 denoising steps, append the current
 block's K/V (fused RoPE + append kernel) and attend its queries over
 [sink, 3 window blocks, current] (bf16 MFMA attention kernel); then evict the
-oldest window block and commit the current one (index remaps).  Inputs are
-seeded synthetic N(0,1)*0.5 bf16 tensors of the workload's shapes, resident in
-HBM before timing.
+oldest window block and commit the current one (index remaps).  Workload
+variants: TwinCache, 720p relative time, block-sparse (tile mask + sparse
+kernel), variable-length blocks, and frame-aligned editing (the chunk's source
+frames staged once, each query also sees its own instant's source frame).
+Inputs are seeded synthetic N(0,1)*0.5 bf16 tensors of the workload's shapes,
+resident in HBM before timing.
 
 Prints ONE JSON line.  `value` = attention TFLOP per chunk / wall time per
 chunk (everything in the step counted in the time).  `roofline` is the
@@ -29,7 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 PEAK_HBM_GBPS = 8000.0
 
-WORKLOADS = {"c2": 2, "c3": 3, "c4": 4, "c5": 5, "c6": 6}
+WORKLOADS = {"c2": 2, "c3": 3, "c4": 4, "c5": 5, "c6": 6, "c7": 7}
 
 
 def attn_flops(B, H, d, n_keys):
@@ -63,12 +66,14 @@ def cpu_baseline(w, sample_heads):
     import oracle.stream as ostream
     n = w.n_sink + w.n_window + 1
     st = ostream.Stream(w)
-    st.slot_inputs(n, 1)                          # warm the input cache (draws are not the oracle)
+    q, slots = st.slot_inputs(n, 1)               # warm the input cache (draws are not the oracle)
     t0 = time.perf_counter()
     st.call(n, 1, heads=list(range(sample_heads)))
     dt = time.perf_counter() - t0
-    keys = (w.n_sink + w.n_window + 1) * w.block_tokens
-    flops = attn_flops(w.block_tokens, sample_heads, w.head_dim, keys)
+    # keys each query sees: every history and current key, plus one source frame when editing
+    keys = sum(k.shape[0] for role, _, k, _ in slots if role != "source")
+    keys += w.lat_h * w.lat_w if slots[-1][0] == "source" else 0
+    flops = attn_flops(q.shape[0], sample_heads, w.head_dim, keys)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     model = ""
     try:
@@ -79,7 +84,7 @@ def cpu_baseline(w, sample_heads):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "cpu_model": model, "nproc": os.cpu_count(),
             "sample": f"one steady-state call (chunk {n}, step 1), {sample_heads} of {w.n_heads} heads, "
-                      f"all {w.block_tokens} queries x {keys} keys, fp64 numpy; {dt:.1f} s",
+                      f"all {q.shape[0]} queries x {keys} keys, fp64 numpy; {dt:.1f} s",
             "seconds": dt}
 
 
@@ -120,7 +125,7 @@ def main():
     cfg = CacheConfig(n_heads=w.n_heads, head_dim=w.head_dim, frames_per_block=w.frames, lat_h=w.lat_h,
                       lat_w=w.lat_w, n_sink=w.n_sink, n_window=w.n_window, twin=w.twin,
                       sparse=w.sparse_keep is not None, dtype=w.dtype, rope_theta=w.rope_theta,
-                      policy=w.policy)
+                      policy=w.policy, editing=w.editing)
     dev = "cuda"
     torch.cuda.init()
     stream = torch.cuda.current_stream()
@@ -130,9 +135,10 @@ def main():
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
 
-    varlen = w.frame_pattern is not None
+    # per-block lengths: a frame pattern, or an editing stream's reference block
+    varlen = w.frame_pattern is not None or w.editing
     hw = w.lat_h * w.lat_w
-    frame_counts = sorted(set(w.frame_pattern)) if varlen else [w.frames]
+    frame_counts = sorted({synth.frames_of(w, b) for b in range(64)})
 
     def draw(frames):
         return (torch.randn((frames * hw, H, d), generator=gen, device=dev, dtype=torch.float32)
@@ -141,6 +147,7 @@ def main():
     # two input sets per block length (alternating chunks), resident in HBM before timing
     sets = {f: [[(draw(f), draw(f), draw(f)) for _ in range(T)] for _ in range(2)] for f in frame_counts}
     noisy = {f: [(draw(f), draw(f)) for _ in range(2)] for f in frame_counts}
+    source = {f: [(draw(f), draw(f)) for _ in range(2)] for f in frame_counts} if w.editing else None
     outs = {f: torch.empty((f * hw, H, d), dtype=torch.bfloat16, device=dev) for f in frame_counts}
     nt = -(-B // 128)
 
@@ -172,7 +179,7 @@ def main():
             cache.append("noisy", kn, vn, b, n_frames=frames_of(b) if varlen else None)
         state["block"] += 1
 
-    ev = {"attn": [], "append": [], "mask": []}
+    ev = {"attn": [], "append": [], "mask": [], "source": []}
     last_mask = {}
 
     flops_timed = {"sum": 0.0, "frames": 0}
@@ -182,17 +189,25 @@ def main():
         fb = frames_of(b)
         out = outs[fb]
         if record:
-            keys = (sum(history) + fb) * hw
+            # keys per query: history + current block, plus its own source frame when editing
+            keys = (sum(history) + fb) * hw + (hw if w.editing else 0)
             flops_timed["sum"] += T * attn_flops(fb * hw, H, d, keys)
             flops_timed["frames"] += fb
         for s in range(T):
             q, k, v = sets[fb][b % 2][s]
             if record:
-                e0, e1, em, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+                e0, e1, es, em, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(5))
                 e0.record(stream)
             append_current(k, v, b)
             if record:
                 e1.record(stream)
+            if w.editing and s == 0:   # the chunk's source frames, staged once for all its steps
+                ks, vs = source[fb][b % 2]
+                cache.append("source", ks, vs, b, n_frames=fb)
+                if record:
+                    ev["source"].append((e1, es))
+            if record:
+                es.record(stream)
             step = "final" if s == T - 1 else "intermediate"
             if w.sparse_keep is not None:
                 idx, k_row = cache.build_tile_mask(q, w.sparse_keep)
@@ -207,7 +222,7 @@ def main():
             if record:
                 e2.record(stream)
                 ev["append"].append((e0, e1))
-                ev["mask"].append((e1, em))
+                ev["mask"].append((es, em))
                 ev["attn"].append((em, e2))
         commit()
 
@@ -283,6 +298,7 @@ def main():
                    "n_sink": w.n_sink, "n_window": w.n_window, "steps_per_chunk": T,
                    "latent_grid": [w.frames, w.lat_h, w.lat_w],
                    "frame_pattern": list(w.frame_pattern) if w.frame_pattern else None,
+                   "editing": {"ref_frames": w.ref_frames, "source_frames": "same instant"} if w.editing else None,
                    "parallelism": "single GPU"},
         "latent_frames_per_s": (flops_timed["frames"] / args.steps if varlen else w.frames) / (ms_chunk * 1e-3),
         "frac_of_bf16_peak_step": flops_chunk / (ms_chunk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -309,6 +325,9 @@ def main():
         res["sparse_attention_hbm"] = {"bytes": 2 * q_bytes + kv_bytes,
                                        "gbps": (2 * q_bytes + kv_bytes) / (avg_attn * 1e-3) / 1e9,
                                        "frac": (2 * q_bytes + kv_bytes) / (avg_attn * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    if w.editing:
+        src_ms = [a.elapsed_time(b) for a, b in ev["source"]]
+        res["source_append_ms_per_chunk"] = sum(src_ms) / len(src_ms)
     if args.cpu_heads > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
     else:

@@ -71,8 +71,14 @@ typedef enum { SW_BF16 = 0, SW_F32 = 1 } sw_dtype;
  *                 the staged current block is promoted (no bytes move); with
  *                 pointers, those raw K/V are written as the committed block
  *                 (used to rebuild a cache, e.g. on resume).
- *  SW_KV_NOISY:   (TwinCache only) the noisy copy of the block just committed. */
-typedef enum { SW_KV_CURRENT = 0, SW_KV_CLEAN = 1, SW_KV_NOISY = 2 } sw_kv_kind;
+ *  SW_KV_NOISY:   (TwinCache only) the noisy copy of the block just committed.
+ *  SW_KV_SOURCE:  (editing caches only) the source-video frames of the staged
+ *                 block: block_id and n_frames must be those of the staged
+ *                 current block.  Written into one staging buffer outside the
+ *                 ring; the commit of the block drops it (source frames never
+ *                 enter the history).  Frame-aligned editing attention: Vidu S2
+ *                 paper read, section 2.6 (the editing model). */
+typedef enum { SW_KV_CURRENT = 0, SW_KV_CLEAN = 1, SW_KV_NOISY = 2, SW_KV_SOURCE = 3 } sw_kv_kind;
 
 /* Which TwinCache copy of the history a denoising step reads (blog, "Choice 3"):
  * intermediate steps read the noisy copies, the final step the clean ones.
@@ -101,6 +107,8 @@ typedef struct {
   double rope_theta;        /* RoPE base, > 1 (10000 is the usual value) */
   sw_rope_policy policy;    /* initial relocation policy */
   int32_t tile;             /* block-sparse tile edge; must be 128 */
+  int32_t editing;          /* 0 | 1: frame-aligned editing (a source staging buffer; dense only;
+                               S + W + 2 <= 16) */
 } sw_cache_config;
 
 /* RoPE layout (pages name 3D RoPE over (t, h, w) without details -- Vidu S2
@@ -110,7 +118,7 @@ typedef struct {
  * pos * theta^(-j/P_a). */
 
 typedef struct {
-  int32_t role;          /* 0 sink, 1 window, 2 current */
+  int32_t role;          /* 0 sink, 1 window, 2 current, 3 source (editing) */
   int64_t block_id;
   int32_t physical_slot; /* ring slot holding the block (changes with eviction) */
   int32_t time_base;     /* RoPE time of the block's first frame */
@@ -186,7 +194,11 @@ sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, float keep_frac,
 /* One denoising step's chunk attention for the staged current block:
  *   out[n][h] = softmax_k(<R(p_n) q_n, R(p_k) k> / sqrt(d)) V
  * over keys [sinks, window oldest->newest, current], positions relocated by
- * the current policy.  q_raw [B][H][d] raw (un-rotated) queries (B = tokens of
+ * the current policy.  Editing caches with a staged source block add, for a
+ * query of frame f, the source tokens of frame f only, at the current block's
+ * positions (the source frame of an instant has the target frame's (t, h, w);
+ * Vidu S2 paper read, section 2.6; BloomBook Vidu S2 tutorial, section
+ * "S2-Editing").  The reference image is the first committed block, a sink.  q_raw [B][H][d] raw (un-rotated) queries (B = tokens of
  * the staged block, see sw_cache_append_block_frames); out [B][H][d]
  * in the cache dtype; lse_out (nullable) [H][B] fp32 natural-log sum of
  * exp(score) per query.  tile_idx == NULL: dense; otherwise block-sparse over
@@ -203,7 +215,8 @@ sw_status sw_cache_inspect(const sw_cache* c, sw_slot_info* out, int32_t cap, in
 /* Copy logical slot `logical_slot`'s stored K (rotated at block-local
  * positions) and V back out as token-major [B][H][d] device arrays (cache
  * dtype).  kind: SW_KV_CLEAN or SW_KV_NOISY (history) / SW_KV_CURRENT (the
- * staged block).  For tests and debugging; blocks until copied. */
+ * staged block) / SW_KV_SOURCE (the staged source frames; logical_slot is
+ * ignored for these two).  For tests and debugging; blocks until copied. */
 sw_status sw_cache_read_slot(sw_cache* c, int32_t logical_slot, sw_kv_kind kind, void* k_out,
                              void* v_out);
 

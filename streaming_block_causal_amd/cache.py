@@ -14,7 +14,8 @@ from . import native
 
 _DTYPES = {"bf16": (native.SW_BF16, torch.bfloat16), "f32": (native.SW_F32, torch.float32)}
 _POLICY = {"s1": native.SW_ROPE_S1_RELOCATE, "relative": native.SW_ROPE_RELATIVE_TIME}
-KIND = {"current": native.SW_KV_CURRENT, "clean": native.SW_KV_CLEAN, "noisy": native.SW_KV_NOISY}
+KIND = {"current": native.SW_KV_CURRENT, "clean": native.SW_KV_CLEAN, "noisy": native.SW_KV_NOISY,
+        "source": native.SW_KV_SOURCE}
 STEP = {"intermediate": native.SW_STEP_INTERMEDIATE, "final": native.SW_STEP_FINAL}
 
 
@@ -33,6 +34,7 @@ class CacheConfig:
     rope_theta: float = 10000.0
     policy: str = "s1"
     tile: int = 128
+    editing: bool = False
 
     @property
     def block_tokens(self) -> int:
@@ -43,7 +45,7 @@ class CacheConfig:
             n_heads=self.n_heads, head_dim=self.head_dim, frames_per_block=self.frames_per_block,
             lat_h=self.lat_h, lat_w=self.lat_w, n_sink=self.n_sink, n_window=self.n_window,
             twin=int(self.twin), sparse=int(self.sparse), dtype=_DTYPES[self.dtype][0],
-            rope_theta=self.rope_theta, policy=_POLICY[self.policy], tile=self.tile)
+            rope_theta=self.rope_theta, policy=_POLICY[self.policy], tile=self.tile, editing=int(self.editing))
 
 
 class Cache:
@@ -151,7 +153,10 @@ class Cache:
 
     def read_slot(self, logical_slot: int, kind: str = "clean"):
         info = self.inspect()
-        frames = info[-1]["frames"] if kind == "current" else info[logical_slot]["frames"]
+        if kind in ("current", "source"):
+            frames = self.cur_frames
+        else:
+            frames = info[logical_slot]["frames"]
         k = torch.empty(self.shape_of(frames), dtype=self.torch_dtype, device=self.device)
         v = torch.empty_like(k)
         native.sw_cache_read_slot(self.handle, logical_slot, KIND[kind], k.data_ptr(), v.data_ptr())

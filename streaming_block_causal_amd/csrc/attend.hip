@@ -45,6 +45,7 @@ struct AttnArgs {
   int k_row;
   int B, H, n_pad, nt, hw, lat_w;
   int n_slots;
+  int aligned_last;   // 1: the last slot is frame-aligned (editing source frames)
   float scale_log2;   // log2(e) / sqrt(d)
   int n_qt;           // query tiles per head of this launch
   int n_full;         // workgroups that own a whole query tile
@@ -153,7 +154,9 @@ __device__ __forceinline__ void stage_load(int p, const u16* kbase, const u16* v
 // Workgroups past n_full each take 1/n_split of the key blocks of one of the remaining tiles
 // and write a normalised partial result; merge_kernel combines them.  This fills the last,
 // partial round of the grid instead of leaving most CUs idle.
-template <bool SPARSE, int NW>
+// ALIGN: the last slot is frame-aligned (editing source frames): per tile only the key blocks of
+// the frames its queries belong to, and a key is masked for the queries of other frames.
+template <bool SPARSE, int NW, bool ALIGN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_bf16_kernel(AttnArgs a) {
   constexpr int ROWS = 32 * NW;
@@ -172,42 +175,62 @@ void attend_bf16_kernel(AttnArgs a) {
   for (int q = 0; q < kMaxSlots; ++q)
     if (tid == q) sslot[q] = a.slot[q];
   // dense schedule: every 64-key block of every slot in logical order (slots may hold blocks of
-  // different lengths)
-  int dense_total = 0;
+  // different lengths); a frame-aligned last slot contributes only the blocks of the frames this
+  // tile's queries belong to (below)
+  int dense_total = 0, aligned_count = 0;
 #pragma unroll
-  for (int q = 0; q < kMaxSlots; ++q)
-    if (q < a.n_slots) dense_total += (a.slot[q].count + KB - 1) / KB;
+  for (int q = 0; q < kMaxSlots; ++q) {
+    if (q < a.n_slots && !(ALIGN && q == a.n_slots - 1)) dense_total += (a.slot[q].count + KB - 1) / KB;
+    if (q == a.n_slots - 1) aligned_count = a.slot[q].count;
+  }
   const RopeTab rt = a.rt;
   const int B = a.B, n_pad = a.n_pad, n_slots = a.n_slots, nt = a.nt;
   const float scale_log2 = a.scale_log2;
   __syncthreads();
 
   const int nkb = (B + KB - 1) / KB;   // sparse: every slot holds B keys
-  const int total = SPARSE ? 2 * a.k_row : dense_total;
-  int tile, i0 = 0, i1 = total, piece = -1;
+  int tile, part = 0, piece = -1;
   if ((int)blockIdx.x < a.n_full) {
     tile = xcd_remap(blockIdx.x, a.n_full);
   } else {
     piece = xcd_remap(blockIdx.x - a.n_full, gridDim.x - a.n_full);
-    const int part = piece % a.n_split;
+    part = piece % a.n_split;
     tile = a.n_full + piece / a.n_split;
+  }
+  const int h = tile / a.n_qt, qt = tile - h * a.n_qt;
+  // frame-aligned slot: key blocks [al_lo, al_hi) cover the frames of rows qt*ROWS .. (last row)
+  int al_lo = 0, al_hi = 0;
+  if (ALIGN) {
+    const int r0 = qt * ROWS, r1 = min(B, r0 + ROWS);
+    al_lo = (r0 / a.hw) * a.hw / KB;
+    al_hi = (min(aligned_count, ((r1 - 1) / a.hw + 1) * a.hw) + KB - 1) / KB;
+    dense_total += al_hi - al_lo;
+  }
+  const int total = SPARSE ? 2 * a.k_row : dense_total;
+  int i0 = 0, i1 = total;
+  if (piece >= 0) {
     i0 = part * total / a.n_split;
     i1 = (part + 1) * total / a.n_split;
   }
-  const int h = tile / a.n_qt, qt = tile - h * a.n_qt;
   const int qrow = qt * ROWS + wave * 32 + ln;
   const bool qvalid = qrow < B;
   const int qf = qrow / a.hw;
   const int qrem = qrow - qf * a.hw;
   const int qh = qrem / a.lat_w, qw = qrem - qh * a.lat_w;
   const u16* qp = static_cast<const u16*>(a.q) + ((size_t)qrow * a.H + h) * D;
+  // frame of key j = floor((j + 0.5) / hw) in fp32: exact, since j < 65536 keeps the rounding error
+  // below 0.01 / hw while (j + 0.5) / hw is at least 0.5 / hw from an integer
+  const float inv_hw = 1.0f / (float)a.hw;
 
   f32x16 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  // running max starts at a finite floor, not -inf: a lane whose keys so far were all masked (a
+  // frame-aligned block of another frame opening a key range) then gets alpha = 1 and p = 0
+  // instead of exp2(-inf - -inf) = NaN when another lane of the wave rescales
+  float m_run = -3.0e38f, l_run = 0.f;
   bf16x8 qb[8];
   load_q<kTimeJ, 8>(rt, qp, qvalid, qf, qh, qw, hf, 0, qb);
 
@@ -248,7 +271,7 @@ void attend_bf16_kernel(AttnArgs a) {
   };
 
   // ---- S^T = K Q^T for 64 keys: two 32x32 tiles, lane holds 16 keys of query ln
-  auto qk = [&](const u16* kl, int kvalid, f32x16& s0, f32x16& s1, const u16* nkb, const u16* nvb, u16* kdst,
+  auto qk = [&](const u16* kl, int kvalid, int afirst, f32x16& s0, f32x16& s1, const u16* nkb, const u16* nvb, u16* kdst,
                 u16* vdst) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -290,6 +313,14 @@ void attend_bf16_kernel(AttnArgs a) {
         const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
         if (key >= kvalid) s0[r] = -INFINITY;
         if (key + 32 >= kvalid) s1[r] = -INFINITY;
+      }
+    }
+    if (afirst >= 0) {   // frame-aligned slot: key afirst + i is seen only by queries of its frame
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = afirst + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if ((int)(((float)key + 0.5f) * inv_hw) != qf) s0[r] = -INFINITY;
+        if ((int)(((float)(key + 32) + 0.5f) * inv_hw) != qf) s1[r] = -INFINITY;
       }
     }
   };
@@ -349,20 +380,22 @@ void attend_bf16_kernel(AttnArgs a) {
   // a slot's key count is read (from LDS, made scalar) only when the cursor enters the slot, and
   // schedule, slot and key count stay in scalar registers.
   int csl = 0, ckb = 0, ccnt = 0, cnb = 0;
+  bool calign = false;
   auto enter = [&](int l) {
     csl = l;
-    ckb = 0;
+    calign = ALIGN && l == n_slots - 1;
     ccnt = __builtin_amdgcn_readfirstlane(sslot[l].count);
-    cnb = (ccnt + KB - 1) / KB;
+    ckb = calign ? al_lo : 0;
+    cnb = calign ? al_hi : (ccnt + KB - 1) / KB;
   };
   if (!SPARSE) {
     enter(0);
     int rem = i0;
-    while (rem >= cnb && csl + 1 < n_slots) {
-      rem -= cnb;
+    while (rem >= cnb - ckb && csl + 1 < n_slots) {
+      rem -= cnb - ckb;
       enter(csl + 1);
     }
-    ckb = rem;
+    ckb += rem;
   }
   // the schedule entry at or after position q (q is left on it): slot, block, keys in the block
   auto lookup = [&](int& q, int& sl, int& kb, int& kv) {
@@ -401,6 +434,7 @@ void attend_bf16_kernel(AttnArgs a) {
   // from buffer cb while block n + 1 is requested into the next buffer
   auto step = [&](const int cb) {
     const int sl = bsl[0], kvalid = bkv[0];
+    const int afirst = (ALIGN && sl == n_slots - 1) ? bkb[0] * KB : -1;
     auto sync = [&]() {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of block n has landed
       // ... and everyone's has; the buffer block n + 1 goes to (that of block n + 1 - NBUF) is
@@ -416,7 +450,7 @@ void attend_bf16_kernel(AttnArgs a) {
       cur_slot = sl;
       load_q<0, kTimeJ>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, qb);
     }
-    qk(kbuf[cb], kvalid, s0, s1, nk, nv, kbuf[(cb + 1) % NBUF], vbuf[(cb + 1) % NBUF]);
+    qk(kbuf[cb], kvalid, afirst, s0, s1, nk, nv, kbuf[(cb + 1) % NBUF], vbuf[(cb + 1) % NBUF]);
     pend = true;
     pend_buf = cb;
     // look the schedule up one block further while the MFMAs drain
@@ -537,7 +571,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
   float qr[DD], acc[DD];
 #pragma unroll
   for (int i = 0; i < DD; ++i) acc[i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -3.0e38f, l_run = 0.f;   // finite floor: a fully masked sub-block gives alpha = 1
   const float scale = a.scale_log2;
 
   for (int sl = 0; sl < a.n_slots; ++sl) {
@@ -556,14 +590,20 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
     const float* kbase = static_cast<const float*>(sslot[sl].k) + (size_t)h * a.n_pad * DD;
     const float* vbase = static_cast<const float*>(sslot[sl].v) + (size_t)h * a.n_pad * DD;
     const int count = sslot[sl].count;
-    for (int k0 = 0; k0 < count; k0 += KBF) {
+    // a frame-aligned last slot: only the frames of this workgroup's rows, key by key below (the
+    // range starts on a multiple of KBF so that every staged sub-block stays inside the slot)
+    const bool al = a.aligned_last && sl == a.n_slots - 1;
+    const int r_first = blockIdx.x * 64, r_last = min(a.B, r_first + 64) - 1;
+    const int k_lo = al ? (r_first / a.hw) * a.hw / KBF * KBF : 0;
+    const int k_hi = al ? min(count, (r_last / a.hw + 1) * a.hw) : count;
+    for (int k0 = k_lo; k0 < k_hi; k0 += KBF) {
       __syncthreads();
       for (int i = tid; i < KBF * DD; i += 64) {
         kl[i / DD][i % DD] = kbase[(size_t)k0 * DD + i];
         vl[i / DD][i % DD] = vbase[(size_t)k0 * DD + i];
       }
       __syncthreads();
-      const int nk = min(KBF, count - k0);
+      const int nk = min(KBF, k_hi - k0);
       float sc[KBF];
       float mx = -INFINITY;
 #pragma unroll
@@ -571,7 +611,8 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
         float dot = 0.f;
 #pragma unroll
         for (int i = 0; i < DD; ++i) dot = fmaf(qr[i], kl[j][i], dot);
-        sc[j] = j < nk ? dot * scale : -INFINITY;
+        const bool seen = j < nk && (!al || (k0 + j) / a.hw == qf);
+        sc[j] = seen ? dot * scale : -INFINITY;
         mx = fmaxf(mx, sc[j]);
       }
       const float m_new = fmaxf(m_run, mx);
@@ -625,11 +666,15 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
   a.hw = g.lat_h * g.lat_w;
   a.lat_w = g.lat_w;
   a.n_slots = n_slots;
+  a.aligned_last = slots[n_slots - 1].aligned ? 1 : 0;
+  for (int l = 0; l + 1 < n_slots; ++l)
+    if (slots[l].aligned) return hipErrorInvalidValue;   // only the last slot may be frame-aligned
+  if (a.aligned_last && (tile_idx || n_slots < 2)) return hipErrorInvalidValue;
   a.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)g.d));
   a.rt = rt;
   a.part_o = plan.part_o;
   a.part_lse = plan.part_lse;
-  for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0, 0};
+  for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0, 0, 0};
   if (bf16) {
     if (g.d != 128) return hipErrorInvalidValue;
     // tail split: whole rounds of resident workgroups own whole tiles; the tiles of a last,
@@ -667,19 +712,25 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
       a.n_qt = g.nt;
       a.n_full = g.nt * g.H;
       a.n_split = 0;
-      hipLaunchKernelGGL((attend_bf16_kernel<true, 4>), dim3(a.n_full), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attend_bf16_kernel<true, 4, false>), dim3(a.n_full), dim3(256), 0, stream, a);
       return hipGetLastError();
     }
     constexpr int NW = kDenseWaves;
     constexpr int ROWS = 32 * NW;
     a.n_qt = (g.B + ROWS - 1) / ROWS;
     const int conc = NW == 4 ? 2 * plan.cus : plan.cus;   // workgroups resident at once
-    int blocks = 0;
-    for (int l = 0; l < n_slots; ++l) blocks += (slots[l].count + KB - 1) / KB;
+    int blocks = 0;   // key blocks every tile has (a frame-aligned slot adds more per tile)
+    for (int l = 0; l < n_slots; ++l)
+      if (!slots[l].aligned) blocks += (slots[l].count + KB - 1) / KB;
     const int tail = plan_split(a.n_qt * g.H, conc, ROWS, blocks);
     const int split = a.n_split;
-    hipLaunchKernelGGL((attend_bf16_kernel<false, NW>), dim3(a.n_full + tail * split), dim3(64 * NW), 0, stream,
-                       a);
+    // the frame-aligned (editing) variant is its own instantiation: the plain kernel keeps its code
+    if (a.aligned_last)
+      hipLaunchKernelGGL((attend_bf16_kernel<false, NW, true>), dim3(a.n_full + tail * split), dim3(64 * NW), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((attend_bf16_kernel<false, NW, false>), dim3(a.n_full + tail * split), dim3(64 * NW), 0,
+                         stream, a);
     if (split) hipLaunchKernelGGL((merge_kernel<ROWS>), dim3(tail, ROWS / kMergeRows), dim3(256), 0, stream, a);
   } else {
     if (tile_idx) return hipErrorInvalidValue;

@@ -67,6 +67,7 @@ struct Layout {
   int pt, ph, pw;
   size_t table_floats;
   size_t ws_bytes;       // partial results of split attention tiles (bf16 caches)
+  size_t src_bytes;      // editing: the source-frame staging buffer (K and V of one block)
   size_t total;
 };
 
@@ -98,6 +99,11 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
   if (c.dtype == SW_F32 && c.head_dim != 64 && c.head_dim != 128)
     return fail(SW_ERR_UNSUPPORTED, "fp32 kernels are built for head_dim 64 or 128 (got %d)", c.head_dim);
   if (c.sparse && c.dtype != SW_BF16) return fail(SW_ERR_UNSUPPORTED, "block-sparse needs bf16");
+  if (c.editing != 0 && c.editing != 1) return fail(SW_ERR_INVALID_ARG, "editing must be 0 or 1");
+  if (c.editing && c.sparse) return fail(SW_ERR_UNSUPPORTED, "frame-aligned editing attention is dense only");
+  if (c.editing && c.n_sink + c.n_window + 2 > kMaxSlots)
+    return fail(SW_ERR_SHAPE, "n_sink + n_window + 2 = %d exceeds %d with editing", c.n_sink + c.n_window + 2,
+                kMaxSlots);
   // the bf16 attention kernel re-rotates only the first 24 pairs per slot: time pairs must fit
   if (c.dtype == SW_BF16 && (c.head_dim / 2) - 2 * ((c.head_dim / 2) / 3) > 24)
     return fail(SW_ERR_UNSUPPORTED, "time RoPE pairs exceed 24");
@@ -128,8 +134,9 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
                     ? align256((size_t)kSplitRows * g.d * sizeof(float)) +
                           align256((size_t)kSplitRows * sizeof(float))
                     : 0;
+  L->src_bytes = c.editing ? 2 * L->kv_bytes : 0;
   L->total = (size_t)L->P * copies * (2 * L->kv_bytes + L->pooled_bytes) +
-             align256(L->table_floats * sizeof(float)) + L->ws_bytes;
+             align256(L->table_floats * sizeof(float)) + L->ws_bytes + L->src_bytes;
   return SW_OK;
 }
 
@@ -155,6 +162,9 @@ struct sw_cache {
   int64_t last_commit;
   bool noisy_due;
   Entry noisy_entry;
+  char* ks;            // editing: source-frame K/V staging buffer (outside the ring)
+  char* vs;
+  bool src_staged;     // source frames of the staged block are in ks/vs
   sw_rope_policy policy;
   SplitPlan plan;
 };
@@ -287,6 +297,9 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
     c->plan.part_lse = L.ws_bytes ? reinterpret_cast<float*>(p + align256((size_t)kSplitRows * L.g.d * sizeof(float)))
                                   : nullptr;
     c->plan.max_rows = L.ws_bytes ? kSplitRows : 0;
+    p += L.ws_bytes;
+    c->ks = L.src_bytes ? p : nullptr;
+    c->vs = L.src_bytes ? p + L.kv_bytes : nullptr;
     int dev = 0, cus = 0;
     hipError_t de = hipGetDevice(&dev);
     if (de == hipSuccess) de = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -326,6 +339,8 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
   c->last_commit = -1;
   c->noisy_due = false;
   c->noisy_entry = Entry{-1, -1, 0};
+  c->src_staged = false;
+  if (dry) c->ks = c->vs = nullptr;
   c->policy = cfg->policy;
   if (dry) c->plan = SplitPlan{0, 0, nullptr, nullptr};
   *out = c;
@@ -415,6 +430,7 @@ sw_status sw_cache_append_block_frames(sw_cache* c, sw_kv_kind kind, const void*
         }
       }
       const int frames = promote ? c->staged_frames : n_frames;
+      c->src_staged = false;   // source frames are consumed with their block, never kept
       if (promote) {
         c->staged = false;
         c->staged_id = -1;
@@ -434,6 +450,25 @@ sw_status sw_cache_append_block_frames(sw_cache* c, sw_kv_kind kind, const void*
           c->noisy_entry = e;
         }
       }
+      return SW_OK;
+    }
+    case SW_KV_SOURCE: {
+      if (!c->cfg.editing) return fail(SW_ERR_STATE, "source frames need an editing cache (editing = 1)");
+      sw_status st = check_ptr(k_raw, "k_raw");
+      if (st == SW_OK) st = check_ptr(v_raw, "v_raw");
+      if (st != SW_OK) return st;
+      if (c->noisy_due) return fail(SW_ERR_STATE, "the noisy copy of block %lld must be appended first",
+                                    (long long)c->noisy_entry.block);
+      if (!c->staged) return fail(SW_ERR_STATE, "source frames belong to the staged block: stage it first");
+      if (block_id != c->staged_id)
+        return fail(SW_ERR_STATE, "staged block is %lld, source frames given for %lld", (long long)c->staged_id,
+                    (long long)block_id);
+      if (n_frames != c->staged_frames)
+        return fail(SW_ERR_STATE, "block %lld is staged with %d frames, its source with %d", (long long)block_id,
+                    c->staged_frames, n_frames);
+      st = write_block(c, k_raw, v_raw, c->ks, c->vs, nullptr, n_frames);
+      if (st != SW_OK) return st;
+      c->src_staged = true;
       return SW_OK;
     }
     case SW_KV_NOISY: {
@@ -532,6 +567,7 @@ sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step, con
   if (c->noisy_due) return fail(SW_ERR_STATE, "a noisy append is due");
   if (tile_idx) {
     if (c->cfg.dtype != SW_BF16) return fail(SW_ERR_UNSUPPORTED, "block-sparse attention needs bf16");
+    if (c->src_staged) return fail(SW_ERR_UNSUPPORTED, "frame-aligned editing attention is dense only");
     if (k_row < 1) return fail(SW_ERR_INVALID_ARG, "k_row must be >= 1 with a tile list");
     if (!all_full(c)) return fail(SW_ERR_UNSUPPORTED, "block-sparse attention needs full-length blocks");
   }
@@ -545,12 +581,15 @@ sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step, con
   for (int l = 0; l + 1 < n_slots; ++l) {
     const int p = hist[l].phys;
     slots[l] = SlotPtrs{noisy ? c->kn[p] : c->kc[p], noisy ? c->vn[p] : c->vc[p], b.back() - b[l],
-                        tokens_of(c, hist[l].frames)};
+                        tokens_of(c, hist[l].frames), 0};
   }
-  slots[n_slots - 1] = SlotPtrs{c->kc[c->staging], c->vc[c->staging], 0, tokens_of(c, c->staged_frames)};
+  slots[n_slots - 1] = SlotPtrs{c->kc[c->staging], c->vc[c->staging], 0, tokens_of(c, c->staged_frames), 0};
+  int n_all = n_slots;
+  if (c->src_staged)   // the source frames sit at the current block's positions, frame-aligned
+    slots[n_all++] = SlotPtrs{c->ks, c->vs, 0, tokens_of(c, c->staged_frames), 1};
   Geometry gq = c->L.g;   // the queries are the staged block's tokens
   gq.B = tokens_of(c, c->staged_frames);
-  const hipError_t e = launch_attend(gq, c->rt, c->cfg.dtype == SW_BF16, q_raw, slots, n_slots, tile_idx, k_row,
+  const hipError_t e = launch_attend(gq, c->rt, c->cfg.dtype == SW_BF16, q_raw, slots, n_all, tile_idx, k_row,
                                      out, lse_out, c->plan, c->stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return SW_OK;
@@ -562,9 +601,18 @@ sw_status sw_cache_inspect(const sw_cache* c, sw_slot_info* out, int32_t cap, in
   const std::vector<Entry> hist = history(c);
   const std::vector<int> b = bases_of(c);
   const int ns = (int)c->sinks.size();
-  const int count = (int)hist.size() + (c->staged ? 1 : 0);
+  const int count = (int)hist.size() + (c->staged ? 1 : 0) + (c->src_staged ? 1 : 0);
   for (int l = 0; l < count && l < cap; ++l) {
     sw_slot_info& s = out[l];
+    if (l == (int)hist.size() + 1) {   // source frames of the staged block
+      s.role = 3;
+      s.block_id = c->staged_id;
+      s.physical_slot = -1;
+      s.twin_complete = 1;
+      s.frames = c->staged_frames;
+      s.time_base = b.back();
+      continue;
+    }
     if (l < (int)hist.size()) {
       s.role = l < ns ? 0 : 1;
       s.block_id = hist[l].block;
@@ -592,6 +640,15 @@ sw_status sw_cache_read_slot(sw_cache* c, int32_t logical_slot, sw_kv_kind kind,
   if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache holds no data");
   const std::vector<Entry> hist = history(c);
   int phys, frames;
+  if (kind == SW_KV_SOURCE) {
+    if (!c->src_staged) return fail(SW_ERR_STATE, "no staged source frames");
+    Geometry g = c->L.g;
+    g.B = tokens_of(c, c->staged_frames);
+    hipError_t e = launch_unpack(g, c->cfg.dtype == SW_BF16, c->ks, c->vs, k_out, v_out, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_fail(e, "read-back");
+    return SW_OK;
+  }
   if (kind == SW_KV_CURRENT) {
     if (!c->staged) return fail(SW_ERR_STATE, "no staged current block");
     phys = c->staging;

@@ -31,6 +31,8 @@ struct SlotPtrs {
   const void* v;   // bf16: V^T [H][d][n_pad] (keys permuted in groups of 16); fp32: V [H][n_pad][d]
   int delta;       // time base of the current block minus this slot's
   int count;       // tokens of the slot's block (<= n_pad)
+  int aligned;     // 1: frame-aligned (editing source) -- key j is seen only by the queries of its
+                   // frame, j / (lat_h * lat_w); must be the last slot
 };
 
 // K1: rotate K at block-local positions, store K and V head-major, pad rows zeroed,

@@ -20,7 +20,7 @@ SW_OK, SW_ERR_INVALID_ARG, SW_ERR_SHAPE, SW_ERR_STATE, SW_ERR_CAPACITY, SW_ERR_U
 STATUS_NAMES = ["SW_OK", "SW_ERR_INVALID_ARG", "SW_ERR_SHAPE", "SW_ERR_STATE", "SW_ERR_CAPACITY",
                 "SW_ERR_UNSUPPORTED", "SW_ERR_HIP"]
 SW_BF16, SW_F32 = 0, 1
-SW_KV_CURRENT, SW_KV_CLEAN, SW_KV_NOISY = 0, 1, 2
+SW_KV_CURRENT, SW_KV_CLEAN, SW_KV_NOISY, SW_KV_SOURCE = 0, 1, 2, 3
 SW_STEP_INTERMEDIATE, SW_STEP_FINAL = 0, 1
 SW_ROPE_S1_RELOCATE, SW_ROPE_RELATIVE_TIME = 0, 1
 
@@ -32,7 +32,7 @@ class sw_cache_config(ctypes.Structure):
         ("n_sink", ctypes.c_int32), ("n_window", ctypes.c_int32),
         ("twin", ctypes.c_int32), ("sparse", ctypes.c_int32),
         ("dtype", ctypes.c_int), ("rope_theta", ctypes.c_double), ("policy", ctypes.c_int),
-        ("tile", ctypes.c_int32),
+        ("tile", ctypes.c_int32), ("editing", ctypes.c_int32),
     ]
 
 
@@ -158,7 +158,7 @@ def sw_cache_inspect(handle: int, cap: int = 16):
     arr = (sw_slot_info * cap)()
     n = ctypes.c_int32()
     _check(lib().sw_cache_inspect(handle, arr, cap, ctypes.byref(n)), "sw_cache_inspect")
-    return [dict(role=("sink", "window", "current")[s.role], block_id=s.block_id, physical_slot=s.physical_slot,
+    return [dict(role=("sink", "window", "current", "source")[s.role], block_id=s.block_id, physical_slot=s.physical_slot,
                  time_base=s.time_base, twin_complete=bool(s.twin_complete), frames=s.frames)
             for s in arr[:min(cap, n.value)]]
 

@@ -21,7 +21,7 @@ def config_for(w: synth.Workload):
     return CacheConfig(n_heads=w.n_heads, head_dim=w.head_dim, frames_per_block=w.frames, lat_h=w.lat_h,
                        lat_w=w.lat_w, n_sink=w.n_sink, n_window=w.n_window, twin=w.twin,
                        sparse=w.sparse_keep is not None, dtype=w.dtype, rope_theta=w.rope_theta,
-                       policy=w.policy, tile=w.tile)
+                       policy=w.policy, tile=w.tile, editing=w.editing)
 
 
 def to_dev(w: synth.Workload, stored: np.ndarray, device="cuda"):
