@@ -309,7 +309,8 @@ def main():
         "latency_flatness": flat,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(args.workload),
-                     "kernel": "attend_bf16_kernel<true, 4>" if w.sparse_keep else "attend_bf16_kernel<false, 8>",
+                     "kernel": ("attend_bf16_kernel<true, 4, false>" if w.sparse_keep else
+                                "attend_bf16_kernel<false, 8, true>" if w.editing else "attend_bf16_kernel<false, 8, false>"),
                      "flops_per_launch": flops_call},
     }
     if w.sparse_keep is not None:
