@@ -98,6 +98,8 @@ def main():
                     help="heads in the oracle sample, about 1 s of CPU time each at 540p (0 = skip)")
     ap.add_argument("--flat-chunks", type=int, default=0, metavar="N",
                     help="after the timed steps, time N more chunks one by one and report the latency slope")
+    ap.add_argument("--graph", action="store_true",
+                    help="after the eager timing, record one chunk graph per ring phase and time their replays")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (scales PMC byte counters)")
     args = ap.parse_args()
@@ -128,7 +130,9 @@ def main():
                       policy=w.policy, editing=w.editing)
     dev = "cuda"
     torch.cuda.init()
-    stream = torch.cuda.current_stream()
+    # a side stream (the NULL stream cannot be recorded into a graph); torch's own work follows it
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
     cache = Cache(cfg, device=dev, stream=stream)
     B, H, d, T = w.block_tokens, w.n_heads, w.head_dim, w.n_steps
     shape = (B, H, d)
@@ -210,7 +214,7 @@ def main():
                 es.record(stream)
             step = "final" if s == T - 1 else "intermediate"
             if w.sparse_keep is not None:
-                idx, k_row = cache.build_tile_mask(q, w.sparse_keep)
+                idx, k_row = cache.build_tile_mask(q, w.sparse_keep, out=mask_buf["idx"], k_cap=mask_buf["k"])
                 last_mask["idx"] = idx
                 if record:
                     em.record(stream)
@@ -232,6 +236,10 @@ def main():
         q, k, v = sets[frames_of(state["block"])][state["block"] % 2][T - 1]
         append_current(k, v, state["block"])
         commit()
+    mask_buf = {}
+    if w.sparse_keep is not None:   # steady-state budget; the buffer is reused (no allocation per call)
+        mask_buf["k"] = cache.mask_budget(w.sparse_keep)
+        mask_buf["idx"] = torch.empty((H, nt, mask_buf["k"]), dtype=torch.int32, device=dev)
     for _ in range(args.warmup):
         chunk(False)
     torch.cuda.synchronize()
@@ -241,6 +249,8 @@ def main():
         chunk(True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    if w.sparse_keep is not None:   # the last timed mask (later phases reuse the buffer)
+        last_mask["idx"] = mask_buf["idx"].clone()
 
     flat = None
     if args.flat_chunks > 0:
@@ -257,6 +267,35 @@ def main():
         slope = sum((i - xm) * (y - ym) for i, y in enumerate(lat)) / max(sum((i - xm) ** 2 for i in range(n)), 1e-30)
         flat = {"chunks": n, "first_block": state["block"] - n, "mean_ms": ym,
                 "slope_pct_of_mean_per_100_chunks": 100.0 * slope * 100.0 / ym}
+
+    graph_rec = None
+    if args.graph:
+        if w.frame_pattern is not None:
+            graph_rec = {"skipped": "block lengths follow a pattern: the ring layout does not repeat"}
+        else:
+            # one recorded chunk per ring phase (the recording only runs host bookkeeping), then
+            # replays in turn: the chunk's appends, masks and attention calls of all its steps
+            period = cache.ring_period()
+            graphs = []
+            for _ in range(period):
+                cache.graph_begin()
+                chunk(False)
+                graphs.append(cache.graph_end())
+            n_rep = max(args.steps, period)
+            for i in range(period):                      # warm-up replays
+                graphs[i].launch()
+            torch.cuda.synchronize()
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            for i in range(n_rep):
+                graphs[i % period].launch()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            ms_graph = g0.elapsed_time(g1) / n_rep
+            graph_rec = {"chunks": n_rep, "ring_period": period, "ms_per_step": ms_graph,
+                         "eager_ms_per_step": dt / args.steps * 1e3}
+            for g in graphs:
+                g.close()
 
     attn_ms = [a.elapsed_time(b) for a, b in ev["attn"]]
     mask_ms = [a.elapsed_time(b) for a, b in ev["mask"]]
@@ -326,6 +365,10 @@ def main():
         res["sparse_attention_hbm"] = {"bytes": 2 * q_bytes + kv_bytes,
                                        "gbps": (2 * q_bytes + kv_bytes) / (avg_attn * 1e-3) / 1e9,
                                        "frac": (2 * q_bytes + kv_bytes) / (avg_attn * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    if graph_rec is not None:
+        if "ms_per_step" in graph_rec:
+            graph_rec["value"] = flops_chunk / (graph_rec["ms_per_step"] * 1e-3) / 1e12
+        res["graph_replay"] = graph_rec
     if w.editing:
         src_ms = [a.elapsed_time(b) for a, b in ev["source"]]
         res["source_append_ms_per_chunk"] = sum(src_ms) / len(src_ms)

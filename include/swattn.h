@@ -220,6 +220,40 @@ sw_status sw_cache_inspect(const sw_cache* c, sw_slot_info* out, int32_t cap, in
 sw_status sw_cache_read_slot(sw_cache* c, int32_t logical_slot, sw_kv_kind kind, void* k_out,
                              void* v_out);
 
+/* ---- graph replay of a chunk's launches -------------------------------------
+ * The pages' stack replays fused kernels with graphs (Vidu S2 paper read, section
+ * 2.4; "Vidu S2 vs PixVerse R2" blog, section "Choice 4: where the speed comes
+ * from").  sw_graph_begin starts capturing the cache's stream (thread-local
+ * capture mode); the append, tile-mask and attention calls that follow are
+ * recorded, not run, while their host bookkeeping (commit, evict, time bases)
+ * takes effect at once; sw_graph_end instantiates the recording.  A replay
+ * reruns the recorded kernels with the recorded arguments: the same input and
+ * output addresses, ring slots and time bases.  In steady state (full window,
+ * full-length blocks) the ring layout repeats every n_window + 1 chunks, so the
+ * graphs of n_window + 1 consecutive chunks, replayed in turn, continue the
+ * stream; the host's block ids do not advance during replays.  Calls that wait
+ * for the device (sw_cache_create, sw_cache_read_slot) fail while capturing.
+ * No memory is allocated or cleared inside a recording. */
+typedef struct sw_graph sw_graph; /* opaque, library-owned */
+
+/* Start capturing the cache's stream.  SW_ERR_STATE if already capturing or
+ * metadata-only; SW_ERR_HIP if the stream cannot be captured (e.g. the NULL
+ * stream). */
+sw_status sw_graph_begin(sw_cache* c);
+
+/* End the capture begun by sw_graph_begin and instantiate it into *out. */
+sw_status sw_graph_end(sw_cache* c, sw_graph** out);
+
+/* Replay a graph on hip_stream (a hipStream_t; NULL = the stream it was
+ * captured from).  Asynchronous, like the calls it recorded. */
+sw_status sw_graph_launch(sw_graph* g, void* hip_stream);
+
+/* Free a graph (after the replays that use it have completed). */
+sw_status sw_graph_destroy(sw_graph* g);
+
+/* Chunks after which the ring layout repeats in steady state (n_window + 1). */
+sw_status sw_cache_ring_period(const sw_cache* c, int32_t* period);
+
 #ifdef __cplusplus
 }
 #endif

@@ -161,3 +161,35 @@ class Cache:
         v = torch.empty_like(k)
         native.sw_cache_read_slot(self.handle, logical_slot, KIND[kind], k.data_ptr(), v.data_ptr())
         return k, v
+
+    # ---- graph replay (see sw_graph_begin) ------------------------------------------
+    def ring_period(self) -> int:
+        return native.sw_cache_ring_period(self.handle)
+
+    def graph_begin(self):
+        """Start recording this cache's stream; pass `out=` to attend while recording (no allocation)."""
+        native.sw_graph_begin(self.handle)
+
+    def graph_end(self) -> "Graph":
+        return Graph(native.sw_graph_end(self.handle))
+
+
+class Graph:
+    """An instantiated recording of library calls; launch() replays it on the recorded stream."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+
+    def launch(self, stream: Optional[torch.cuda.Stream] = None):
+        native.sw_graph_launch(self.handle, stream.cuda_stream if stream is not None else None)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            native.sw_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -167,6 +167,12 @@ struct sw_cache {
   bool src_staged;     // source frames of the staged block are in ks/vs
   sw_rope_policy policy;
   SplitPlan plan;
+  bool capturing;      // between sw_graph_begin and sw_graph_end
+};
+
+struct sw_graph {
+  hipGraphExec_t exec;
+  hipStream_t stream;   // the stream it was captured from
 };
 
 namespace {
@@ -340,6 +346,7 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
   c->noisy_due = false;
   c->noisy_entry = Entry{-1, -1, 0};
   c->src_staged = false;
+  c->capturing = false;
   if (dry) c->ks = c->vs = nullptr;
   c->policy = cfg->policy;
   if (dry) c->plan = SplitPlan{0, 0, nullptr, nullptr};
@@ -349,7 +356,62 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
 
 sw_status sw_cache_destroy(sw_cache* c) {
   if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  if (c->capturing) return fail(SW_ERR_STATE, "a graph capture is in progress; end it first");
   delete c;
+  return SW_OK;
+}
+
+sw_status sw_graph_begin(sw_cache* c) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache cannot launch kernels");
+  if (c->capturing) return fail(SW_ERR_STATE, "already capturing");
+  const hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e, "begin capture");
+  c->capturing = true;
+  return SW_OK;
+}
+
+sw_status sw_graph_end(sw_cache* c, sw_graph** out) {
+  if (!c || !out) return fail(SW_ERR_INVALID_ARG, "cache or out is NULL");
+  if (!c->capturing) return fail(SW_ERR_STATE, "no capture in progress");
+  c->capturing = false;
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(c->stream, &graph);
+  if (e != hipSuccess) return hip_fail(e, "end capture");
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  hipGraphDestroy(graph);
+  if (e != hipSuccess) return hip_fail(e, "graph instantiation");
+  sw_graph* g = new (std::nothrow) sw_graph();
+  if (!g) {
+    hipGraphExecDestroy(exec);
+    return fail(SW_ERR_CAPACITY, "host allocation failed");
+  }
+  g->exec = exec;
+  g->stream = c->stream;
+  *out = g;
+  return SW_OK;
+}
+
+sw_status sw_graph_launch(sw_graph* g, void* hip_stream) {
+  if (!g) return fail(SW_ERR_INVALID_ARG, "graph is NULL");
+  const hipStream_t s = hip_stream ? static_cast<hipStream_t>(hip_stream) : g->stream;
+  const hipError_t e = hipGraphLaunch(g->exec, s);
+  if (e != hipSuccess) return hip_fail(e, "graph launch");
+  return SW_OK;
+}
+
+sw_status sw_graph_destroy(sw_graph* g) {
+  if (!g) return fail(SW_ERR_INVALID_ARG, "graph is NULL");
+  const hipError_t e = hipGraphExecDestroy(g->exec);
+  delete g;
+  if (e != hipSuccess) return hip_fail(e, "graph destruction");
+  return SW_OK;
+}
+
+sw_status sw_cache_ring_period(const sw_cache* c, int32_t* period) {
+  if (!c || !period) return fail(SW_ERR_INVALID_ARG, "cache or period is NULL");
+  *period = c->cfg.n_window + 1;
   return SW_OK;
 }
 
@@ -638,6 +700,7 @@ sw_status sw_cache_read_slot(sw_cache* c, int32_t logical_slot, sw_kv_kind kind,
   if (st == SW_OK) st = check_ptr(v_out, "v_out");
   if (st != SW_OK) return st;
   if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache holds no data");
+  if (c->capturing) return fail(SW_ERR_STATE, "read-back waits for the device: not while capturing a graph");
   const std::vector<Entry> hist = history(c);
   int phys, frames;
   if (kind == SW_KV_SOURCE) {

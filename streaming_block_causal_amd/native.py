@@ -74,6 +74,11 @@ def lib() -> ctypes.CDLL:
             "sw_chunk_attend": ([H, P, ctypes.c_int, P, I32, P, P], ctypes.c_int),
             "sw_cache_inspect": ([H, ctypes.POINTER(sw_slot_info), I32, ctypes.POINTER(I32)], ctypes.c_int),
             "sw_cache_read_slot": ([H, I32, ctypes.c_int, P, P], ctypes.c_int),
+            "sw_graph_begin": ([H], ctypes.c_int),
+            "sw_graph_end": ([H, ctypes.POINTER(H)], ctypes.c_int),
+            "sw_graph_launch": ([H, P], ctypes.c_int),
+            "sw_graph_destroy": ([H], ctypes.c_int),
+            "sw_cache_ring_period": ([H, ctypes.POINTER(I32)], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -165,3 +170,27 @@ def sw_cache_inspect(handle: int, cap: int = 16):
 
 def sw_cache_read_slot(handle: int, logical_slot: int, kind: int, k_ptr: int, v_ptr: int) -> None:
     _check(lib().sw_cache_read_slot(handle, logical_slot, kind, k_ptr, v_ptr), "sw_cache_read_slot")
+
+
+def sw_graph_begin(handle: int) -> None:
+    _check(lib().sw_graph_begin(handle), "sw_graph_begin")
+
+
+def sw_graph_end(handle: int) -> int:
+    g = ctypes.c_void_p()
+    _check(lib().sw_graph_end(handle, ctypes.byref(g)), "sw_graph_end")
+    return g.value
+
+
+def sw_graph_launch(graph: int, stream_ptr: Optional[int] = None) -> None:
+    _check(lib().sw_graph_launch(graph, stream_ptr or None), "sw_graph_launch")
+
+
+def sw_graph_destroy(graph: int) -> None:
+    _check(lib().sw_graph_destroy(graph), "sw_graph_destroy")
+
+
+def sw_cache_ring_period(handle: int) -> int:
+    p = ctypes.c_int32()
+    _check(lib().sw_cache_ring_period(handle, ctypes.byref(p)), "sw_cache_ring_period")
+    return p.value
