@@ -98,6 +98,9 @@ def main():
                     help="heads in the oracle sample, about 1 s of CPU time each at 540p (0 = skip)")
     ap.add_argument("--flat-chunks", type=int, default=0, metavar="N",
                     help="after the timed steps, time N more chunks one by one and report the latency slope")
+    ap.add_argument("--fused-qkv", action="store_true",
+                    help="stage each step from a packed QKV projection output through the fused "
+                         "RMSNorm + RoPE + append epilogue (the attention then reads the normalised q)")
     ap.add_argument("--graph", action="store_true",
                     help="after the eager timing, record one chunk graph per ring phase and time their replays")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -149,7 +152,19 @@ def main():
                 * w.scale).to(torch.bfloat16)
 
     # two input sets per block length (alternating chunks), resident in HBM before timing
-    sets = {f: [[(draw(f), draw(f), draw(f)) for _ in range(T)] for _ in range(2)] for f in frame_counts}
+    if args.fused_qkv:
+        # packed [B][3][H][d] projection outputs; q/k/v below are views of them (the plain path is
+        # unchanged) and the epilogue writes the normalised q into its own buffer
+        def packed(f):
+            return (torch.randn((f * hw, 3, H, d), generator=gen, device=dev, dtype=torch.float32)
+                    * w.scale).to(torch.bfloat16)
+        qkv_sets = {f: [[packed(f) for _ in range(T)] for _ in range(2)] for f in frame_counts}
+        sets = {f: [[(x[:, 0], x[:, 1], x[:, 2]) for x in qkv_sets[f][i]] for i in range(2)] for f in frame_counts}
+        gq = torch.rand(d, generator=gen, device=dev) + 0.5
+        gk = torch.rand(d, generator=gen, device=dev) + 0.5
+        qn = {f: torch.empty((f * hw, H, d), dtype=torch.bfloat16, device=dev) for f in frame_counts}
+    else:
+        sets = {f: [[(draw(f), draw(f), draw(f)) for _ in range(T)] for _ in range(2)] for f in frame_counts}
     noisy = {f: [(draw(f), draw(f)) for _ in range(2)] for f in frame_counts}
     source = {f: [(draw(f), draw(f)) for _ in range(2)] for f in frame_counts} if w.editing else None
     outs = {f: torch.empty((f * hw, H, d), dtype=torch.bfloat16, device=dev) for f in frame_counts}
@@ -202,7 +217,11 @@ def main():
             if record:
                 e0, e1, es, em, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(5))
                 e0.record(stream)
-            append_current(k, v, b)
+            if args.fused_qkv:
+                q = cache.append_qkv(qkv_sets[fb][b % 2][s], gq, gk, 1e-6, b, q_out=qn[fb],
+                                     n_frames=fb)
+            else:
+                append_current(k, v, b)
             if record:
                 e1.record(stream)
             if w.editing and s == 0:   # the chunk's source frames, staged once for all its steps
@@ -233,8 +252,13 @@ def main():
     # fill the cache to steady state (appends and commits only, so every attention launch
     # below -- and in a profiler trace of this script -- has the full key set), then warm up
     while state["block"] < n_slots_full - 1:
-        q, k, v = sets[frames_of(state["block"])][state["block"] % 2][T - 1]
-        append_current(k, v, state["block"])
+        fb0 = frames_of(state["block"])
+        q, k, v = sets[fb0][state["block"] % 2][T - 1]
+        if args.fused_qkv:
+            cache.append_qkv(qkv_sets[fb0][state["block"] % 2][T - 1], gq, gk, 1e-6, state["block"],
+                             q_out=qn[fb0], n_frames=fb0)
+        else:
+            append_current(k, v, state["block"])
         commit()
     mask_buf = {}
     if w.sparse_keep is not None:   # steady-state budget; the buffer is reused (no allocation per call)
@@ -318,7 +342,8 @@ def main():
     srt = sorted(attn_ms)
     p50, p95 = srt[len(srt) // 2], srt[min(len(srt) - 1, int(0.95 * len(srt)))]
     achieved = flops_call / (avg_attn * 1e-3) / 1e12
-    append_bytes = 2 * 2 * B * H * d * 2          # read raw K,V + write K,V (bf16)
+    # plain: read raw K, V + write K, V^T; fused epilogue: read q, k, v + write q, K, V^T (bf16)
+    append_bytes = (6 if args.fused_qkv else 4) * B * H * d * 2
     avg_app = sum(app_ms) / len(app_ms)
     res = {
         "metric": "chunk-attention TFLOP/s + latent frames/s (sink+window KV), % of MFMA peak",
@@ -338,6 +363,7 @@ def main():
                    "latent_grid": [w.frames, w.lat_h, w.lat_w],
                    "frame_pattern": list(w.frame_pattern) if w.frame_pattern else None,
                    "editing": {"ref_frames": w.ref_frames, "source_frames": "same instant"} if w.editing else None,
+                   "qkv_epilogue": "fused RMSNorm + RoPE + append" if args.fused_qkv else None,
                    "parallelism": "single GPU"},
         "latent_frames_per_s": (flops_timed["frames"] / args.steps if varlen else w.frames) / (ms_chunk * 1e-3),
         "frac_of_bf16_peak_step": flops_chunk / (ms_chunk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

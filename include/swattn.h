@@ -166,6 +166,21 @@ sw_status sw_cache_append_block(sw_cache* c, sw_kv_kind kind, const void* k_raw,
 sw_status sw_cache_append_block_frames(sw_cache* c, sw_kv_kind kind, const void* k_raw,
                                        const void* v_raw, int64_t block_id, int32_t n_frames);
 
+/* Stage the current block from the packed output of a QKV projection, with the
+ * per-head RMSNorm of q and k fused into the append (Vidu S2 paper read,
+ * section 2.4: adjacent operators such as RMSNorm and elementwise work fused
+ * into one kernel).  qkv_raw [B][3][H][d] in the cache dtype (q, k, v of a
+ * token side by side, B = n_frames*lat_h*lat_w); gamma_q, gamma_k device fp32
+ * [d]; for every token and head x -> x / sqrt(mean_d(x^2) + eps) * gamma.  The
+ * normalised q is written to q_out [B][H][d] (cache dtype, un-rotated: pass it
+ * to sw_chunk_attend); the normalised k, rotated at block-local positions, and
+ * v become the staged current block exactly as SW_KV_CURRENT stages raw K/V.
+ * Same staging rules as SW_KV_CURRENT; SW_ERR_UNSUPPORTED unless head_dim is
+ * 128; SW_ERR_INVALID_ARG for NULL pointers, eps < 0 or n_frames out of
+ * range.  One kernel, one pass over HBM. */
+sw_status sw_cache_append_qkv(sw_cache* c, const void* qkv_raw, const float* gamma_q, const float* gamma_k,
+                              float eps, void* q_out, int64_t block_id, int32_t n_frames);
+
 /* Drop the oldest window block (index remap, no bytes move).  Sinks are never
  * evicted.  SW_ERR_STATE if the window is empty or a NOISY append is due. */
 sw_status sw_cache_evict(sw_cache* c);

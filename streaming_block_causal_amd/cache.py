@@ -111,6 +111,22 @@ class Cache:
         if kind == "current":
             self.cur_frames = self.cfg.frames_per_block if n_frames is None else n_frames
 
+    def append_qkv(self, qkv: torch.Tensor, gamma_q: torch.Tensor, gamma_k: torch.Tensor, eps: float,
+                   block_id: int, q_out: Optional[torch.Tensor] = None, n_frames: Optional[int] = None):
+        """Stage the current block from a packed QKV projection output [B][3][H][d], RMSNorm of q
+        and k fused in (see sw_cache_append_qkv); returns the normalised q [B][H][d]."""
+        n_frames = self.cfg.frames_per_block if n_frames is None else n_frames
+        shape = self.shape_of(n_frames)
+        if q_out is None and self.device is not None:
+            q_out = torch.empty(shape, dtype=self.torch_dtype, device=self.device)
+        qkv_shape = (shape[0], 3, shape[1], shape[2])
+        native.sw_cache_append_qkv(self.handle, self._tensor(qkv, "qkv", shape=qkv_shape),
+                                   self._tensor(gamma_q, "gamma_q", torch.float32, (shape[2],)),
+                                   self._tensor(gamma_k, "gamma_k", torch.float32, (shape[2],)), eps,
+                                   self._tensor(q_out, "q_out", shape=shape), block_id, n_frames)
+        self.cur_frames = n_frames
+        return q_out
+
     def evict(self):
         native.sw_cache_evict(self.handle)
 

@@ -14,6 +14,15 @@
 //
 // One workgroup per (128-token tile, head); HBM-bound: reads B*H*d raw K and V
 // once, writes them once.
+//
+// The fused QKV epilogue (NORM) reads the packed output of a QKV projection
+// ([B][3][H][d]: q, k, v of a token side by side), normalises q and k per head
+// (RMSNorm over d with per-channel weights: x / sqrt(mean(x^2) + eps) * g),
+// writes the normalised q token-major for the attention call, and stores the
+// normalised, rotated k and the v like the plain append -- one pass over HBM for
+// what would otherwise be two norm kernels and the append (Vidu S2 paper read,
+// section 2.4: adjacent operators such as RMSNorm and elementwise work fused
+// into one kernel).
 #include "device_common.h"
 
 namespace swattn {
@@ -28,7 +37,31 @@ struct AppendArgs {
   float* pooled;
   int B, H, n_pad, nt, hw, lat_w;
   RopeTab rt;
+  size_t row_stride;    // elements from one token's k (or v) to the next: H*d, or 3*H*d packed
+  const void* q_raw;    // NORM only: q of the packed projection output, normalised into q_out
+  void* q_out;          // [B][H][d]
+  const float* gq;      // [d] RMSNorm weights of q and k
+  const float* gk;
+  float eps;
 };
+
+// sum over the 16 lanes that hold one row (aligned groups of 16 within the wave)
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// x[0..8) of a row (this lane's 8 channels starting at c0) *= rsqrt(mean over the row of x^2 + eps) * g
+__device__ __forceinline__ void rms_scale8(float* x, const float* g, int c0, int D, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+  ss = row16_sum(ss);
+  const float inv = 1.0f / __builtin_sqrtf(ss / (float)D + eps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = x[i] * inv * g[c0 + i];
+}
 
 template <bool BF16>
 struct Elem;
@@ -68,8 +101,9 @@ struct Elem<false> {
   }
 };
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool NORM>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  static_assert(!NORM || D / 8 == 16, "the row reduction assumes 16 lanes per row");
   typedef typename Elem<BF16>::T T;
   constexpr int GPR = D / 8;              // 8-element groups per row
   constexpr int ITEMS = kTile * GPR / 256;
@@ -93,8 +127,15 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int row = (tid + 256 * it) / GPR;
     const int r = j * kTile + row;
     float x[8];
+    if (NORM && r < a.B) {   // q: normalise, store token-major (the attention call rotates it)
+      float y[8];
+      Elem<BF16>::load8(static_cast<const T*>(a.q_raw) + (size_t)r * a.row_stride + (size_t)h * D + grp * 8, y);
+      rms_scale8(y, a.gq, grp * 8, D, a.eps);
+      Elem<BF16>::store8(static_cast<T*>(a.q_out) + ((size_t)r * a.H + h) * D + grp * 8, y);
+    }
     if (r < a.B) {
-      Elem<BF16>::load8(kr + ((size_t)r * a.H + h) * D + grp * 8, x);
+      Elem<BF16>::load8(kr + (size_t)r * a.row_stride + (size_t)h * D + grp * 8, x);
+      if (NORM) rms_scale8(x, a.gk, grp * 8, D, a.eps);
       const int f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -116,12 +157,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     if (BF16) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (r < a.B) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(vr) +
-                                                       ((size_t)r * a.H + h) * D + grp * 8);
+                                                       (size_t)r * a.row_stride + (size_t)h * D + grp * 8);
       *reinterpret_cast<uint4*>(&vl[row][grp * 8]) = v;
     } else {
       float y[8];
       if (r < a.B) {
-        Elem<BF16>::load8(vr + ((size_t)r * a.H + h) * D + grp * 8, y);
+        Elem<BF16>::load8(vr + (size_t)r * a.row_stride + (size_t)h * D + grp * 8, y);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = 0.f;
@@ -194,16 +235,35 @@ hipError_t launch_append(const Geometry& g, const RopeTab& rt, bool bf16, const 
                          const void* v_raw, void* k_dst, void* v_dst, float* pooled_dst,
                          hipStream_t stream) {
   AppendArgs a{k_raw, v_raw, k_dst, v_dst, pooled_dst, g.B, g.H, g.n_pad, g.nt,
-               g.lat_h * g.lat_w, g.lat_w, rt};
+               g.lat_h * g.lat_w, g.lat_w, rt, (size_t)g.H * g.d, nullptr, nullptr, nullptr, nullptr, 0.f};
   const dim3 grid(g.nt, g.H), block(256);
   if (bf16 && g.d == 128) {
-    hipLaunchKernelGGL((append_kernel<128, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<128, true, false>), grid, block, 0, stream, a);
   } else if (!bf16 && g.d == 128) {
-    hipLaunchKernelGGL((append_kernel<128, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<128, false, false>), grid, block, 0, stream, a);
   } else if (!bf16 && g.d == 64) {
-    hipLaunchKernelGGL((append_kernel<64, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<64, false, false>), grid, block, 0, stream, a);
   } else {
     return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append_qkv(const Geometry& g, const RopeTab& rt, bool bf16, const void* qkv,
+                             const float* gamma_q, const float* gamma_k, float eps, void* q_out,
+                             void* k_dst, void* v_dst, float* pooled_dst, hipStream_t stream) {
+  const size_t hd = (size_t)g.H * g.d;
+  const size_t esz = bf16 ? 2 : 4;
+  const char* base = static_cast<const char*>(qkv);
+  AppendArgs a{base + hd * esz, base + 2 * hd * esz, k_dst, v_dst, pooled_dst, g.B, g.H, g.n_pad, g.nt,
+               g.lat_h * g.lat_w, g.lat_w, rt, 3 * hd, base, q_out, gamma_q, gamma_k, eps};
+  const dim3 grid(g.nt, g.H), block(256);
+  if (bf16 && g.d == 128) {
+    hipLaunchKernelGGL((append_kernel<128, true, true>), grid, block, 0, stream, a);
+  } else if (!bf16 && g.d == 128) {
+    hipLaunchKernelGGL((append_kernel<128, false, true>), grid, block, 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;   // the row reduction is built for d = 128
   }
   return hipGetLastError();
 }

@@ -233,6 +233,22 @@ sw_status check_ptr(const void* p, const char* name) {
   return SW_OK;
 }
 
+// may block `block_id` of `n_frames` frames be staged as the current block now?
+sw_status check_stage(const sw_cache* c, int64_t block_id, int n_frames) {
+  if (c->noisy_due) return fail(SW_ERR_STATE, "the noisy copy of block %lld must be appended first",
+                                (long long)c->noisy_entry.block);
+  if (c->staged && block_id != c->staged_id)
+    return fail(SW_ERR_STATE, "block %lld is staged; commit it before staging block %lld",
+                (long long)c->staged_id, (long long)block_id);
+  if (c->have_commit && block_id <= c->last_commit)
+    return fail(SW_ERR_STATE, "block %lld is not newer than the last commit %lld", (long long)block_id,
+                (long long)c->last_commit);
+  if (c->staged && n_frames != c->staged_frames)
+    return fail(SW_ERR_STATE, "block %lld is staged with %d frames, not %d", (long long)block_id,
+                c->staged_frames, n_frames);
+  return SW_OK;
+}
+
 sw_status write_block(sw_cache* c, const void* k, const void* v, char* kd, char* vd, float* pd, int frames) {
   if (c->dry) return SW_OK;
   Geometry g = c->L.g;   // the slot keeps its capped stride (n_pad); the block fills its first rows
@@ -437,18 +453,8 @@ sw_status sw_cache_append_block_frames(sw_cache* c, sw_kv_kind kind, const void*
     case SW_KV_CURRENT: {
       sw_status st = check_ptr(k_raw, "k_raw");
       if (st == SW_OK) st = check_ptr(v_raw, "v_raw");
+      if (st == SW_OK) st = check_stage(c, block_id, n_frames);
       if (st != SW_OK) return st;
-      if (c->noisy_due) return fail(SW_ERR_STATE, "the noisy copy of block %lld must be appended first",
-                                    (long long)c->noisy_entry.block);
-      if (c->staged && block_id != c->staged_id)
-        return fail(SW_ERR_STATE, "block %lld is staged; commit it before staging block %lld",
-                    (long long)c->staged_id, (long long)block_id);
-      if (c->have_commit && block_id <= c->last_commit)
-        return fail(SW_ERR_STATE, "block %lld is not newer than the last commit %lld", (long long)block_id,
-                    (long long)c->last_commit);
-      if (c->staged && n_frames != c->staged_frames)
-        return fail(SW_ERR_STATE, "block %lld is staged with %d frames, not %d", (long long)block_id,
-                    c->staged_frames, n_frames);
       const int s = c->staging;
       st = write_block(c, k_raw, v_raw, c->kc[s], c->vc[s], c->pc[s], n_frames);
       if (st != SW_OK) return st;
@@ -553,6 +559,38 @@ sw_status sw_cache_append_block_frames(sw_cache* c, sw_kv_kind kind, const void*
     }
   }
   return fail(SW_ERR_INVALID_ARG, "unknown kv kind %d", (int)kind);
+}
+
+sw_status sw_cache_append_qkv(sw_cache* c, const void* qkv_raw, const float* gamma_q, const float* gamma_k,
+                              float eps, void* q_out, int64_t block_id, int32_t n_frames) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  sw_status st = check_ptr(qkv_raw, "qkv_raw");
+  if (st == SW_OK) st = check_ptr(gamma_q, "gamma_q");
+  if (st == SW_OK) st = check_ptr(gamma_k, "gamma_k");
+  if (st == SW_OK) st = check_ptr(q_out, "q_out");
+  if (st != SW_OK) return st;
+  if (block_id < 0) return fail(SW_ERR_INVALID_ARG, "block_id must be >= 0");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(SW_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (n_frames < 1 || n_frames > c->cfg.frames_per_block)
+    return fail(SW_ERR_INVALID_ARG, "n_frames %d outside [1, %d]", n_frames, c->cfg.frames_per_block);
+  if (c->cfg.sparse && n_frames != c->cfg.frames_per_block)
+    return fail(SW_ERR_UNSUPPORTED, "block-sparse caches hold full-length blocks only");
+  if (c->cfg.head_dim != 128) return fail(SW_ERR_UNSUPPORTED, "the QKV epilogue is built for head_dim 128");
+  st = check_stage(c, block_id, n_frames);
+  if (st != SW_OK) return st;
+  const int s = c->staging;
+  if (!c->dry) {
+    Geometry g = c->L.g;
+    g.B = tokens_of(c, n_frames);
+    g.nt = (g.B + kTile - 1) / kTile;
+    const hipError_t e = launch_append_qkv(g, c->rt, c->cfg.dtype == SW_BF16, qkv_raw, gamma_q, gamma_k, eps,
+                                           q_out, c->kc[s], c->vc[s], c->pc[s], c->stream);
+    if (e != hipSuccess) return hip_fail(e, "QKV epilogue kernel launch");
+  }
+  c->staged = true;
+  c->staged_id = block_id;
+  c->staged_frames = n_frames;
+  return SW_OK;
 }
 
 sw_status sw_cache_evict(sw_cache* c) {

@@ -41,6 +41,13 @@ hipError_t launch_append(const Geometry& g, const RopeTab& rt, bool bf16, const 
                          const void* v_raw, void* k_dst, void* v_dst, float* pooled_dst,
                          hipStream_t stream);
 
+// K1 with the QKV epilogue: qkv [B][3][H][d] (q, k, v of a token side by side); q and k are
+// RMS-normalised per head over d with weights gamma_q / gamma_k (fp32 [d]); q goes to q_out
+// [B][H][d], k (then rotated) and v to the slot as in launch_append.  d = 128 only.
+hipError_t launch_append_qkv(const Geometry& g, const RopeTab& rt, bool bf16, const void* qkv,
+                             const float* gamma_q, const float* gamma_k, float eps, void* q_out,
+                             void* k_dst, void* v_dst, float* pooled_dst, hipStream_t stream);
+
 // Work split of the dense bf16 attention grid: the device's CU count sets how many
 // workgroups are resident at once; the workspace holds max_rows partial query rows.
 struct SplitPlan {

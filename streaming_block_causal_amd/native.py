@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "sw_cache_destroy": ([H], ctypes.c_int),
             "sw_cache_append_block": ([H, ctypes.c_int, P, P, I64], ctypes.c_int),
             "sw_cache_append_block_frames": ([H, ctypes.c_int, P, P, I64, I32], ctypes.c_int),
+            "sw_cache_append_qkv": ([H, P, P, P, F32, P, I64, I32], ctypes.c_int),
             "sw_cache_evict": ([H], ctypes.c_int),
             "sw_rope_relocate": ([H, ctypes.c_int], ctypes.c_int),
             "sw_tile_mask_budget": ([H, F32, ctypes.POINTER(I32)], ctypes.c_int),
@@ -130,6 +131,12 @@ def sw_cache_append_block_frames(handle: int, kind: int, k_ptr: Optional[int], v
                                  block_id: int, n_frames: int):
     _check(lib().sw_cache_append_block_frames(handle, kind, k_ptr or None, v_ptr or None, block_id, n_frames),
            "sw_cache_append_block_frames")
+
+
+def sw_cache_append_qkv(handle: int, qkv_ptr: int, gq_ptr: int, gk_ptr: int, eps: float, q_out_ptr: int,
+                        block_id: int, n_frames: int) -> None:
+    _check(lib().sw_cache_append_qkv(handle, qkv_ptr or None, gq_ptr or None, gk_ptr or None, eps,
+                                     q_out_ptr or None, block_id, n_frames), "sw_cache_append_qkv")
 
 
 def sw_cache_evict(handle: int) -> None:
