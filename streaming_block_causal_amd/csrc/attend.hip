@@ -307,7 +307,11 @@ void attend_bf16_kernel(AttnArgs a) {
       if (jj < NST) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // one staging load
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (kvalid < KB) {   // last block of its slot: keys past the block's end do not exist
+    // The masks below are taken only by a few blocks per tile.  The scheduling barrier (an
+    // intrinsic with side effects) keeps the compiler from if-converting them into selects that
+    // every block would execute (about 80 VALU instructions per wave and block).
+    if (__builtin_expect(kvalid < KB, 0)) {   // last block of its slot: keys past its end do not exist
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -315,7 +319,8 @@ void attend_bf16_kernel(AttnArgs a) {
         if (key + 32 >= kvalid) s1[r] = -INFINITY;
       }
     }
-    if (afirst >= 0) {   // frame-aligned slot: key afirst + i is seen only by queries of its frame
+    if (__builtin_expect(afirst >= 0, 0)) {   // frame-aligned slot: key afirst + i is seen only by
+      __builtin_amdgcn_sched_barrier(0);        // the queries of its frame
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = afirst + 8 * (r >> 2) + 4 * hf + (r & 3);
