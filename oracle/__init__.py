@@ -30,9 +30,19 @@ reading of the prose, listed with the other readings in the design notes):
   mean-pooled tile scores on 128x128 tiles with forced tiles.  ``tilemask.py``.
 * Attention itself -- scaled dot-product softmax attention, the textbook
   definition (the pages name attention but print no formula).  ``attention.py``.
+* Variable-length blocks -- blog, section "Choice 5: how people control it":
+  block length follows the control signal up to a cap.  ``rope.py``,
+  ``stream.py``.
+* Frame-aligned editing attention -- paper read, section 2.6 (the editing
+  model); BloomBook Vidu S2 tutorial, section "S2-Editing".  ``stream.py``,
+  ``bruteforce.py``.
+* RMSNorm of q and k fused with the append -- paper read, section 2.4 (kernel
+  fusion).  ``qknorm.py``.
+* fp8 attention -- paper read, section 2.4 (quantised attention chosen per
+  layer); an own E4M3 scheme with power-of-two group scales.  ``fp8.py``.
 
 Pins (tests/test_oracle_*.py) tie each function to something other than itself:
 closed forms, library routines, brute force over the whole stream with an
 explicit block mask, and hand-computed worked examples under tests/golden/.
 """
-from . import attention, bruteforce, cache, rope, stream, tilemask  # noqa: F401
+from . import attention, bruteforce, cache, fp8, qknorm, rope, stream, tilemask  # noqa: F401

@@ -36,7 +36,7 @@ import numpy as np
 
 import synth
 
-from . import attention, cache, rope, tilemask
+from . import attention, cache, fp8, rope, tilemask
 
 
 class Stream:
@@ -147,6 +147,11 @@ def relocated_head(w: synth.Workload, stored: np.ndarray, head: int, base: int) 
 
 def _one_head(job, h):
     w, q, slots, bases, rows = job["w"], job["q"], job["slots"], job["bases"], job["rows"]
+    if w.attn_fp8:
+        if job["kept"] is not None or w.sparse_keep is not None or slots[-1][0] == "source":
+            raise ValueError("fp8 attention is built for the dense stream")
+        o, lse = fp8.attend_head(w, h, q, slots, bases, rows, synth.as_f64)
+        return o, lse, None
     q_rel = relocated_head(w, q, h, bases[-1])
     k_rel = [relocated_head(w, k, h, bases[l]) for l, (_, _, k, _) in enumerate(slots)]
     v_all = np.concatenate([synth.as_f64(w, v[:, h, :]) for (_, _, _, v) in slots], axis=0)

@@ -70,6 +70,7 @@ class Workload:
     frame_pattern: Optional[Tuple[int, ...]] = None   # frames of block b = pattern[b % len]; None: `frames`
     editing: bool = False            # block 0 is the reference, blocks >= 1 carry source frames
     ref_frames: Optional[int] = None  # editing: latent frames of the reference block (None: as block 0)
+    attn_fp8: bool = False           # attention on fp8 (E4M3, power-of-two group scales) Q, K, V
 
     @property
     def block_tokens(self) -> int:
@@ -107,6 +108,9 @@ WORKLOADS: Dict[int, Workload] = {
     7: Workload("c7_540p_editing_bf16", 7, n_heads=24, head_dim=128, frames=3, lat_h=34, lat_w=60,
                 n_sink=1, n_window=3, n_chunks=32, n_steps=4, dtype="bf16", scale=0.5,
                 editing=True, ref_frames=1),
+    # the 540p dense stream with attention on fp8-quantised Q, K, V (inputs still bf16)
+    8: Workload("c8_540p_fp8", 8, n_heads=24, head_dim=128, frames=3, lat_h=34, lat_w=60,
+                n_sink=1, n_window=3, n_chunks=32, n_steps=4, dtype="bf16", scale=0.5, attn_fp8=True),
 }
 
 
