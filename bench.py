@@ -30,9 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
+PEAK_FP8_TFLOPS = 5033.2      # 256 CU x 2.4 GHz x 8192 flop/clk (dense)
 PEAK_HBM_GBPS = 8000.0
 
-WORKLOADS = {"c2": 2, "c3": 3, "c4": 4, "c5": 5, "c6": 6, "c7": 7}
+WORKLOADS = {"c2": 2, "c3": 3, "c4": 4, "c5": 5, "c6": 6, "c7": 7, "c8": 8}
 
 
 def attn_flops(B, H, d, n_keys):
@@ -129,7 +130,8 @@ def main():
     w = synth.WORKLOADS[WORKLOADS[args.workload]]
     cfg = CacheConfig(n_heads=w.n_heads, head_dim=w.head_dim, frames_per_block=w.frames, lat_h=w.lat_h,
                       lat_w=w.lat_w, n_sink=w.n_sink, n_window=w.n_window, twin=w.twin,
-                      sparse=w.sparse_keep is not None, dtype=w.dtype, rope_theta=w.rope_theta,
+                      sparse=w.sparse_keep is not None, dtype="fp8" if w.attn_fp8 else w.dtype,
+                      rope_theta=w.rope_theta,
                       policy=w.policy, editing=w.editing)
     dev = "cuda"
     torch.cuda.init()
@@ -345,6 +347,7 @@ def main():
     # plain: read raw K, V + write K, V^T; fused epilogue: read q, k, v + write q, K, V^T (bf16)
     append_bytes = (6 if args.fused_qkv else 4) * B * H * d * 2
     avg_app = sum(app_ms) / len(app_ms)
+    peak = PEAK_FP8_TFLOPS if w.attn_fp8 else PEAK_BF16_TFLOPS   # the contraction's own dtype
     res = {
         "metric": "chunk-attention TFLOP/s + latent frames/s (sink+window KV), % of MFMA peak",
         "value": flops_chunk / (ms_chunk * 1e-3) / 1e12,
@@ -356,7 +359,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if w.attn_fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "block_tokens": B, "keys": keys, "heads": H, "head_dim": d,
                    "n_sink": w.n_sink, "n_window": w.n_window, "steps_per_chunk": T,
@@ -372,9 +375,10 @@ def main():
         "append_ms_per_call": avg_app,
         "append_gbps": append_bytes / (avg_app * 1e-3) / 1e9,
         "latency_flatness": flat,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(args.workload),
-                     "kernel": ("attend_bf16_kernel<true, 4, false>" if w.sparse_keep else
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": load_traffic(args.workload),
+                     "kernel": ("attend_fp8_kernel<8>" if w.attn_fp8 else
+                                "attend_bf16_kernel<true, 4, false>" if w.sparse_keep else
                                 "attend_bf16_kernel<false, 8, true>" if w.editing else "attend_bf16_kernel<false, 8, false>"),
                      "flops_per_launch": flops_call},
     }

@@ -62,7 +62,14 @@ typedef enum {
   SW_ERR_HIP = 6          /* a HIP runtime call failed (message has the HIP error) */
 } sw_status;
 
-typedef enum { SW_BF16 = 0, SW_F32 = 1 } sw_dtype;
+/* Storage and arithmetic of a cache.  SW_BF16 / SW_F32: inputs, stored K/V and
+ * outputs in that type.  SW_FP8: bf16 inputs and outputs; K (after RoPE) and V
+ * stored as OCP FP8 E4M3 with a power-of-two scale per 32 values, and the
+ * attention multiplies in fp8 on the MFMA units (quantised attention chosen per
+ * layer: Vidu S2 paper read, section 2.4); head_dim 128, dense stream only (no
+ * block-sparse, no editing, no QKV epilogue); sw_cache_read_slot returns the
+ * dequantised values as fp32. */
+typedef enum { SW_BF16 = 0, SW_F32 = 1, SW_FP8 = 2 } sw_dtype;
 
 /* What an append writes.
  *  SW_KV_CURRENT: the current (not yet committed) block's K/V for this

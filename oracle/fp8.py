@@ -15,8 +15,7 @@ scaled fp8 matrix instructions of CDNA4 and is defined here step by step:
 * K is quantised after its rotation at block-local positions (t = frame in the
   block, h, w), in groups of 32 consecutive channels of one key and head.
 * V is quantised per channel and head within each 64-key block, in two groups:
-  the 32 keys whose index inside the block has bit 2 clear, and the 32 with it
-  set.
+  its first 32 keys and its last 32 keys.
 * Q is quantised for each cache slot separately, after its rotation at the
   relocated time of that slot (the query carries the relocation), in groups of
   32 consecutive channels of one query and head.
@@ -68,19 +67,15 @@ def quantize_groups(x: np.ndarray, axis: int = -1, group: int = 32) -> np.ndarra
 
 
 def quantize_v(v: np.ndarray) -> np.ndarray:
-    """V [N, ...] (keys first): per channel, per 64-key block, the keys with index bit 2 clear
-    form one group and those with it set the other.  A short last block pads with zeros."""
+    """V [N, ...] (keys first): per channel, per 64-key block, the first 32 keys form one group
+    and the last 32 the other.  A short last block pads with zeros."""
     v = np.asarray(v, dtype=np.float64)
     n = v.shape[0]
     n64 = -(-n // 64) * 64
     vp = np.zeros((n64,) + v.shape[1:])
     vp[:n] = v
     blk = vp.reshape((n64 // 64, 64) + v.shape[1:])
-    idx = np.arange(64)
-    out = np.empty_like(blk)
-    for half in (0, 1):
-        sel = idx[((idx >> 2) & 1) == half]              # 32 keys of this group, ascending
-        out[:, sel] = quantize_groups(blk[:, sel], axis=1, group=32)
+    out = quantize_groups(blk, axis=1, group=32)          # keys 0..31 and 32..63 of each block
     return out.reshape(vp.shape)[:n]
 
 

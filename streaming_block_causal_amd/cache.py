@@ -12,7 +12,9 @@ import torch
 
 from . import native
 
-_DTYPES = {"bf16": (native.SW_BF16, torch.bfloat16), "f32": (native.SW_F32, torch.float32)}
+# cache dtype -> (C enum, torch dtype of inputs and outputs); fp8 caches take and return bf16
+_DTYPES = {"bf16": (native.SW_BF16, torch.bfloat16), "f32": (native.SW_F32, torch.float32),
+           "fp8": (native.SW_FP8, torch.bfloat16)}
 _POLICY = {"s1": native.SW_ROPE_S1_RELOCATE, "relative": native.SW_ROPE_RELATIVE_TIME}
 KIND = {"current": native.SW_KV_CURRENT, "clean": native.SW_KV_CLEAN, "noisy": native.SW_KV_NOISY,
         "source": native.SW_KV_SOURCE}
@@ -173,7 +175,8 @@ class Cache:
             frames = self.cur_frames
         else:
             frames = info[logical_slot]["frames"]
-        k = torch.empty(self.shape_of(frames), dtype=self.torch_dtype, device=self.device)
+        out_dtype = torch.float32 if self.cfg.dtype == "fp8" else self.torch_dtype   # fp8: dequantised
+        k = torch.empty(self.shape_of(frames), dtype=out_dtype, device=self.device)
         v = torch.empty_like(k)
         native.sw_cache_read_slot(self.handle, logical_slot, KIND[kind], k.data_ptr(), v.data_ptr())
         return k, v

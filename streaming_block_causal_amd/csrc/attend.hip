@@ -644,6 +644,386 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------------------------------
+// fp8 MFMA kernel (dense): Q, K, V in OCP E4M3 with power-of-two scales per 32 values,
+// v_mfma_scale_f32_32x32x64_f8f6f4 (each lane's 32 operand bytes carry that lane's
+// E8M0 scale), fp32 softmax, P rounded to E4M3 (scale 1: p <= 2^8 < 448 under the lazy
+// rescale), fp32 accumulation.  Cache layout: see append_fp8.hip.  Same grid, split and
+// pipeline as the bf16 dense kernel; per 64-key block a wave issues 4 + 4 MFMAs (64
+// channels or 64 keys of contraction each) and reads 8 KB of K and 8 KB of V^T from LDS.
+// The scaled MFMA applies the E8M0 scale of lane half 0 to operand bytes 0-15 of both lane
+// halves (one 32-value group) and that of half 1 to bytes 16-31 (the other group).
+//   QK: A = K tile t (32 keys), lane (key 32t + ln, hf) holds channels 64c + 16hf + [0, 16) in
+//       bytes 0-15 and 64c + 32 + 16hf + [0, 16) in bytes 16-31, so bytes 0-15 of the two halves
+//       are channel group 2c and bytes 16-31 group 2c + 1; lane half hf supplies the scale of
+//       group 2c + hf.  B = Q, the same placement; S^T as in the bf16 kernel.
+//   PV: A = V^T tile t (32 channels), lane (channel 32t + ln, hf) holds the stored positions
+//       32hf + [0, 32) of the block (keys with index bit 2 == hf); B = P^T, lane (query ln, hf)
+//       holds exactly those keys' probabilities: its 16 scores of S^T tile 0 (keys 0..31, the
+//       first V group), then of tile 1 (keys 32..63, the second).
+// LDS rows are XOR-swizzled by 16-byte chunks (K: 128 B rows, chunk c at c ^ (row & 7);
+// V^T: 64 B rows, chunk c at c ^ ((row >> 2) & 3)) so the operand reads are conflict-free.
+// ------------------------------------------------------------------------------------
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int e8m0_of(float amax) {   // smallest e with amax / 2^e <= 448
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (b >> 23) & 255;
+  if (E == 0) return -127;
+  const int e = E - 135 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// Q operand chunks [C0, C1) of one lane: channels 64c + 16hf + [0, 16) and 64c + 32 + 16hf +
+// [0, 16) of its query, rotated at time frame + delta; each half is quantised with the scale of
+// its 32-channel group (the two lane halves exchange their partial maxima); byte c of qsc is
+// the scale this lane supplies (group 2c + hf)
+template <int C0, int C1>
+__device__ __forceinline__ void load_q8(const RopeTab rt, const u16* qp, bool valid, int qf, int qh, int qw, int hf,
+                                        int delta, v8i (&q8)[2], uint32_t& qsc) {
+  const int t = qf + delta;
+#pragma unroll
+  for (int c = C0; c < C1; ++c) {
+    float x[32];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int base = 64 * c + 32 * g + 16 * hf;
+      if (valid) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint4 raw = ldg16(qp + base + 8 * u);
+          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float cs, sn;
+            rope_cs(rt, base / 2 + 4 * u + i, t, qh, qw, cs, sn);
+            const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xffff0000u);
+            x[16 * g + 8 * u + 2 * i] = x0 * cs - x1 * sn;
+            x[16 * g + 8 * u + 2 * i + 1] = x0 * sn + x1 * cs;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[16 * g + i] = 0.f;
+      }
+    }
+    float am[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am[i >> 4] = fmaxf(am[i >> 4], fabsf(x[i]));
+    const int e0 = e8m0_of(swap_halves_max(am[0])), e1 = e8m0_of(swap_halves_max(am[1]));
+    const float sc0 = __uint_as_float((uint32_t)(127 - e0) << 23), sc1 = __uint_as_float((uint32_t)(127 - e1) << 23);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q8[c][i] = (int)pack4_fp8(x[4 * i] * sc0, x[4 * i + 1] * sc0, x[4 * i + 2] * sc0, x[4 * i + 3] * sc0);
+      q8[c][4 + i] = (int)pack4_fp8(x[16 + 4 * i] * sc1, x[17 + 4 * i] * sc1, x[18 + 4 * i] * sc1,
+                                    x[19 + 4 * i] * sc1);
+    }
+    const int e = hf ? e1 : e0;
+    qsc = (qsc & ~(0xffu << (8 * c))) | ((uint32_t)(e + 127) << (8 * c));
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attend_fp8_kernel(AttnArgs a) {
+  constexpr int ROWS = 32 * NW;
+  constexpr int NBUF = 2;
+  static_assert(NW == 8, "one 1 KB K chunk and one V^T chunk per wave and block");
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[NBUF][KB * D];   // 8 KB
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[NBUF][D * KB];   // 8 KB
+  __shared__ SlotPtrs sslot[kMaxSlots];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, ln = lane & 31;
+#pragma unroll
+  for (int q = 0; q < kMaxSlots; ++q)
+    if (tid == q) sslot[q] = a.slot[q];
+  int dense_total = 0;
+#pragma unroll
+  for (int q = 0; q < kMaxSlots; ++q)
+    if (q < a.n_slots) dense_total += (a.slot[q].count + KB - 1) / KB;
+  const RopeTab rt = a.rt;
+  const int B = a.B, n_pad = a.n_pad, n_slots = a.n_slots, H = a.H;
+  const float scale_log2 = a.scale_log2;
+  __syncthreads();
+
+  int tile, part = 0, piece = -1;
+  if ((int)blockIdx.x < a.n_full) {
+    tile = xcd_remap(blockIdx.x, a.n_full);
+  } else {
+    piece = xcd_remap(blockIdx.x - a.n_full, gridDim.x - a.n_full);
+    part = piece % a.n_split;
+    tile = a.n_full + piece / a.n_split;
+  }
+  const int h = tile / a.n_qt, qt = tile - h * a.n_qt;
+  const int total = dense_total;
+  int i0 = 0, i1 = total;
+  if (piece >= 0) {
+    i0 = part * total / a.n_split;
+    i1 = (part + 1) * total / a.n_split;
+  }
+  const int qrow = qt * ROWS + wave * 32 + ln;
+  const bool qvalid = qrow < B;
+  const int qf = qrow / a.hw;
+  const int qrem = qrow - qf * a.hw;
+  const int qh = qrem / a.lat_w, qw = qrem - qh * a.lat_w;
+  const u16* qp = static_cast<const u16*>(a.q) + ((size_t)qrow * a.H + h) * D;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  float m_run = -3.0e38f, l_run = 0.f;   // finite floor, as in the bf16 kernel
+  v8i q8[2];
+  uint32_t qsc = 0x7f7f7f7fu;
+  load_q8<0, 2>(rt, qp, qvalid, qf, qh, qw, hf, 0, q8, qsc);
+
+  // per-lane LDS byte offsets of the operand reads (two 16-byte chunks each)
+  int koff[2][2], voff[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) koff[c][u] = ln * 128 + 16 * ((4 * c + 2 * u + hf) ^ (ln & 7));
+#pragma unroll
+  for (int u = 0; u < 2; ++u) voff[u] = ln * 64 + 16 * ((2 * hf + u) ^ ((ln >> 2) & 3));
+  // staging: wave w moves K rows 8w..8w+7 and V^T rows 16w..16w+15 of the block
+  const int kr = 8 * wave + (lane >> 3), vr = 16 * wave + (lane >> 2);
+  const int stk = kr * D + 16 * ((lane & 7) ^ (kr & 7));
+  const int stv = vr * n_pad + 16 * ((lane & 3) ^ ((vr >> 2) & 3));
+  const size_t kstride = (size_t)n_pad * D;   // bytes per head, K and V^T alike
+
+  // scales (E8M0 bytes) of a block: K -- the lane's key in tiles 0 and 1, shifted so that bytes 0
+  // and 2 are the groups of channel chunks 0 and 1 for its half; V -- the lane's 4 channels
+  auto load_scales = [&](int s, int kb, uint32_t& k0, uint32_t& k1, uint32_t& vs) {
+    const SlotPtrs sp = sslot[s];
+    const uint8_t* kb8 = static_cast<const uint8_t*>(sp.k) + (size_t)H * kstride + (size_t)h * n_pad * 4;
+    const uint8_t* vb8 = static_cast<const uint8_t*>(sp.v) + (size_t)H * kstride + (size_t)h * n_pad * 4;
+    const uint32_t* kp = reinterpret_cast<const uint32_t*>(kb8) + kb * KB + ln;
+    k0 = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(reinterpret_cast<uintptr_t>(kp)) >>
+         (8 * hf);
+    k1 = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(reinterpret_cast<uintptr_t>(kp + 32)) >>
+         (8 * hf);
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(vb8) + (kb * 2 + hf) * 32 + ln;
+    vs = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(reinterpret_cast<uintptr_t>(vp));
+  };
+  auto stage = [&](int s, int kb, int buf) {
+    const SlotPtrs sp = sslot[s];
+    const uint8_t* kg = reinterpret_cast<const uint8_t*>(
+        uniform_ptr(static_cast<const uint8_t*>(sp.k) + h * kstride + (size_t)kb * KB * D));
+    const uint8_t* vg = reinterpret_cast<const uint8_t*>(uniform_ptr(static_cast<const uint8_t*>(sp.v) + h * kstride + kb * KB));
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const __attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(kg + stk)),
+        reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&kbuf[buf][1024 * wave])),
+        16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const __attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(vg + stv)),
+        reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&vbuf[buf][1024 * wave])),
+        16, 0, 0);
+  };
+
+  // ---- S^T = K Q^T for 64 keys: tiles t = 0, 1 (32 keys each), two channel chunks of 64
+  auto qk = [&](const uint8_t* kl, int kvalid, uint32_t k0, uint32_t k1, f32x16& s0, f32x16& s1, bool stage_next,
+                int nsl, int nkb, int nbuf) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = 0.f;
+      s1[r] = 0.f;
+    }
+    v8i kop[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(kl + 4096 * t + koff[c][0]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(kl + 4096 * t + koff[c][1]);
+        kop[c][t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[0][0], q8[0], s0, 0, 0, 0, (int)k0, 0, (int)qsc);
+    // the next block's loads ride along with the MFMAs
+    if (stage_next) stage(nsl, nkb, nbuf);
+    s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[0][1], q8[0], s1, 0, 0, 0, (int)k1, 0, (int)qsc);
+    s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[1][0], q8[1], s0, 0, 0, 2, (int)k0, 1, (int)qsc);
+    s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[1][1], q8[1], s1, 0, 0, 2, (int)k1, 1, (int)qsc);
+    if (__builtin_expect(kvalid < KB, 0)) {   // last block of its slot: keys past its end do not exist
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key >= kvalid) s0[r] = -INFINITY;
+        if (key + 32 >= kvalid) s1[r] = -INFINITY;
+      }
+    }
+  };
+  // ---- online softmax (log2 domain, lazy rescale), P -> E4M3, then O^T += V^T P^T
+  auto sm_pv = [&](const uint8_t* vl, uint32_t vs, f32x16& s0, f32x16& s1) {
+    v8i vop[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(vl + 2048 * t + voff[0]);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(vl + 2048 * t + voff[1]);
+      vop[t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    mx = swap_halves_max(mx) * scale_log2;
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+    }
+    const float mneg = -m_run;
+    float p0[16], p1[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, mneg));
+      p1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, mneg));
+    }
+    v8i p8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p8[i] = (int)pack4_fp8(p0[4 * i], p0[4 * i + 1], p0[4 * i + 2], p0[4 * i + 3]);
+      p8[4 + i] = (int)pack4_fp8(p1[4 * i], p1[4 * i + 1], p1[4 * i + 2], p1[4 * i + 3]);
+    }
+    // row sum of the E4M3 probabilities that multiply V, on the matrix unit: an all-ones A
+    // operand (0x38 = 1.0) gives every row of the product the sum over the 64 keys
+    const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838};
+    const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const f32x16 rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, p8, zero, 0, 0, 0, 127, 0, 127);
+    l_run += rs[0];
+    acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[0], p8, acc[0], 0, 0, 0, (int)vs, 0, 127);
+    acc[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[1], p8, acc[1], 0, 0, 1, (int)vs, 0, 127);
+    acc[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[2], p8, acc[2], 0, 0, 2, (int)vs, 0, 127);
+    acc[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[3], p8, acc[3], 0, 0, 3, (int)vs, 0, 127);
+  };
+  f32x16 s0, s1;
+
+  // dense schedule cursor (as in the bf16 kernel)
+  int csl = 0, ckb = 0, ccnt = 0, cnb = 0;
+  auto enter = [&](int l) {
+    csl = l;
+    ckb = 0;
+    ccnt = __builtin_amdgcn_readfirstlane(sslot[l].count);
+    cnb = (ccnt + KB - 1) / KB;
+  };
+  enter(0);
+  {
+    int rem = i0;
+    while (rem >= cnb && csl + 1 < n_slots) {
+      rem -= cnb;
+      enter(csl + 1);
+    }
+    ckb = rem;
+  }
+  auto lookup = [&](int& q, int& sl, int& kb, int& kv) {
+    if (q < i1) {
+      while (ckb >= cnb && csl + 1 < n_slots) enter(csl + 1);
+      sl = csl;
+      kb = ckb;
+      kv = ccnt - ckb * KB;
+      ++ckb;
+    }
+  };
+  int pos[3], bsl[3] = {0, 0, 0}, bkb[3] = {0, 0, 0}, bkv[3] = {0, 0, 0};
+  {
+    int q = i0;
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      lookup(q, bsl[u], bkb[u], bkv[u]);
+      pos[u] = q;
+      if (q < i1) ++q;
+    }
+  }
+  uint32_t ksc0[NBUF], ksc1[NBUF], vsc[NBUF];
+  // "no block" stages block 0 of slot 0 (a valid address) so that every wave's loads match
+  stage(pos[0] < i1 ? bsl[0] : 0, pos[0] < i1 ? bkb[0] : 0, 0);
+  load_scales(pos[0] < i1 ? bsl[0] : 0, pos[0] < i1 ? bkb[0] : 0, ksc0[0], ksc1[0], vsc[0]);
+  int cur_slot = -1;   // the time channels of Q are rotated for the slot on entry
+  bool pend = false;
+  int pend_buf = 0;
+
+  auto step = [&](const int cb) {
+    const int sl = bsl[0], kvalid = bkv[0];
+    if (pend) sm_pv(vbuf[cb ^ 1], vsc[cb ^ 1], s0, s1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of block n (and its scales)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (sl != cur_slot) {
+      cur_slot = sl;
+      load_q8<0, 1>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, q8, qsc);
+    }
+    const bool has_next = pos[1] < i1;
+    const int nsl = has_next ? bsl[1] : 0, nkb = has_next ? bkb[1] : 0;
+    load_scales(nsl, nkb, ksc0[cb ^ 1], ksc1[cb ^ 1], vsc[cb ^ 1]);
+    qk(kbuf[cb], kvalid, ksc0[cb], ksc1[cb], s0, s1, true, nsl, nkb, cb ^ 1);
+    pend = true;
+    pend_buf = cb;
+    int q = pos[2] < i1 ? pos[2] + 1 : i1, nsl2 = 0, nkb2 = 0, nkv = 0;
+    if (pos[2] < i1) lookup(q, nsl2, nkb2, nkv);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      pos[u] = pos[u + 1];
+      bsl[u] = bsl[u + 1];
+      bkb[u] = bkb[u + 1];
+      bkv[u] = bkv[u + 1];
+    }
+    pos[2] = q;
+    bsl[2] = nsl2;
+    bkb[2] = nkb2;
+    bkv[2] = nkv;
+  };
+  while (pos[0] < i1) {
+    step(0);
+    if (pos[0] >= i1) break;
+    step(1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (pend) sm_pv(vbuf[pend_buf], vsc[pend_buf], s0, s1);
+
+  const float l_tot = l_run;   // both lane halves hold the full row sum (from the matrix unit)
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (piece >= 0) {
+    const int row = wave * 32 + ln;
+    float* po = a.part_o + ((size_t)piece * ROWS + row) * D;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *reinterpret_cast<float4*>(po + 32 * t + 8 * rg + 4 * hf) =
+            make_float4(acc[t][4 * rg] * inv, acc[t][4 * rg + 1] * inv, acc[t][4 * rg + 2] * inv,
+                        acc[t][4 * rg + 3] * inv);
+    if (hf == 0) a.part_lse[(size_t)piece * ROWS + row] = m_run + __log2f(l_tot);
+    return;
+  }
+  if (qvalid) {
+    u16* op = static_cast<u16*>(a.o) + ((size_t)qrow * a.H + h) * D;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = 32 * t + 8 * rg + 4 * hf;
+        uint2 w;
+        w.x = (uint32_t)f2bf(acc[t][4 * rg] * inv) | ((uint32_t)f2bf(acc[t][4 * rg + 1] * inv) << 16);
+        w.y = (uint32_t)f2bf(acc[t][4 * rg + 2] * inv) | ((uint32_t)f2bf(acc[t][4 * rg + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + d0) = w;
+      }
+    if (a.lse && hf == 0) a.lse[(size_t)h * B + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
 }  // namespace
 
 #ifndef SWATTN_DENSE_WAVES
@@ -653,6 +1033,39 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
 constexpr int kDenseWaves = SWATTN_DENSE_WAVES;
 
 
+
+// Work split of a dense grid of `tiles` query tiles (`rows` queries each, `blocks` key blocks
+// each at least) with `conc` workgroups resident at once.  Tail split: whole rounds of resident
+// workgroups own whole tiles; the tiles of a last, partial round are cut into up to kMaxSplit key
+// ranges (only when a whole round exists).  Fewer tiles than resident workgroups (short blocks):
+// every tile is cut so that the pieces fill whole rounds (the smallest cut reaching 95% of the
+// slots, if it gains 5 points).  Sets a.n_full / a.n_split; returns the number of split tiles.
+int plan_split(AttnArgs& a, const SplitPlan& plan, int tiles, int conc, int rows, int blocks) {
+  const int tail = conc > 0 ? tiles % conc : 0;
+  const int max_pieces = plan.part_o ? plan.max_rows / rows : 0;
+  int split = 0;
+  if (plan.part_o && conc > 0 && tail > 0) {
+    if (tiles >= conc) {
+      split = std::min(std::min(kMaxSplit, conc / tail), max_pieces / tail);
+      split = std::min(split, blocks);   // no empty key ranges
+      if (split < 2) split = 0;
+    } else {
+      double best = (double)tiles / conc;
+      for (int sp = 2; sp <= std::min(kMaxSplit, blocks) && tiles * sp <= max_pieces; ++sp) {
+        const int pieces = tiles * sp, rounds = (pieces + conc - 1) / conc;
+        const double util = (double)pieces / ((double)rounds * conc);
+        if (util > best + 0.05) {
+          best = util;
+          split = sp;
+          if (util >= 0.95) break;
+        }
+      }
+    }
+  }
+  a.n_full = split ? tiles - tail : tiles;
+  a.n_split = split;
+  return tail;
+}
 
 hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const void* q,
                          const SlotPtrs* slots, int n_slots, const int32_t* tile_idx, int k_row,
@@ -682,36 +1095,6 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
   for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0, 0, 0};
   if (bf16) {
     if (g.d != 128) return hipErrorInvalidValue;
-    // tail split: whole rounds of resident workgroups own whole tiles; the tiles of a last,
-    // partial round are cut into up to kMaxSplit key ranges (only when a whole round exists)
-    // fewer tiles than resident workgroups (short blocks): every tile is cut so that the pieces
-    // fill whole rounds (the smallest cut reaching 95% of the slots, if it gains 5 points)
-    auto plan_split = [&](int tiles, int conc, int rows, int blocks) {
-      const int tail = conc > 0 ? tiles % conc : 0;
-      const int max_pieces = plan.part_o ? plan.max_rows / rows : 0;
-      int split = 0;
-      if (plan.part_o && conc > 0 && tail > 0) {
-        if (tiles >= conc) {
-          split = std::min(std::min(kMaxSplit, conc / tail), max_pieces / tail);
-          split = std::min(split, blocks);   // no empty key ranges
-          if (split < 2) split = 0;
-        } else {
-          double best = (double)tiles / conc;
-          for (int sp = 2; sp <= std::min(kMaxSplit, blocks) && tiles * sp <= max_pieces; ++sp) {
-            const int pieces = tiles * sp, rounds = (pieces + conc - 1) / conc;
-            const double util = (double)pieces / ((double)rounds * conc);
-            if (util > best + 0.05) {
-              best = util;
-              split = sp;
-              if (util >= 0.95) break;
-            }
-          }
-        }
-      }
-      a.n_full = split ? tiles - tail : tiles;
-      a.n_split = split;
-      return tail;
-    };
     if (tile_idx) {   // block-sparse: 128-query tiles, 4 waves, two workgroups per CU (no split:
                       // the lists are short and the merge costs more than the tail round)
       a.n_qt = g.nt;
@@ -727,7 +1110,7 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
     int blocks = 0;   // key blocks every tile has (a frame-aligned slot adds more per tile)
     for (int l = 0; l < n_slots; ++l)
       if (!slots[l].aligned) blocks += (slots[l].count + KB - 1) / KB;
-    const int tail = plan_split(a.n_qt * g.H, conc, ROWS, blocks);
+    const int tail = plan_split(a, plan, a.n_qt * g.H, conc, ROWS, blocks);
     const int split = a.n_split;
     // the frame-aligned (editing) variant is its own instantiation: the plain kernel keeps its code
     if (a.aligned_last)
@@ -747,6 +1130,41 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
     else
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_fp8(const Geometry& g, const RopeTab& rt, const void* q, const SlotPtrs* slots, int n_slots,
+                             void* out, float* lse, const SplitPlan& plan, hipStream_t stream) {
+  if (n_slots < 1 || n_slots > kMaxSlots || g.d != 128) return hipErrorInvalidValue;
+  for (int l = 0; l < n_slots; ++l)
+    if (slots[l].aligned) return hipErrorInvalidValue;   // frame-aligned slots: bf16 only
+  AttnArgs a;
+  a.q = q;
+  a.o = out;
+  a.lse = lse;
+  a.tile_idx = nullptr;
+  a.k_row = 0;
+  a.B = g.B;
+  a.H = g.H;
+  a.n_pad = g.n_pad;
+  a.nt = g.nt;
+  a.hw = g.lat_h * g.lat_w;
+  a.lat_w = g.lat_w;
+  a.n_slots = n_slots;
+  a.aligned_last = 0;
+  a.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)g.d));
+  a.rt = rt;
+  a.part_o = plan.part_o;
+  a.part_lse = plan.part_lse;
+  for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0, 0, 0};
+  constexpr int NW = 8, ROWS = 32 * NW;
+  a.n_qt = (g.B + ROWS - 1) / ROWS;
+  int blocks = 0;
+  for (int l = 0; l < n_slots; ++l) blocks += (slots[l].count + KB - 1) / KB;
+  const int tail = plan_split(a, plan, a.n_qt * g.H, plan.cus, ROWS, blocks);
+  const int split = a.n_split;
+  hipLaunchKernelGGL((attend_fp8_kernel<NW>), dim3(a.n_full + tail * split), dim3(64 * NW), 0, stream, a);
+  if (split) hipLaunchKernelGGL((merge_kernel<ROWS>), dim3(tail, ROWS / kMergeRows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -88,12 +88,17 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
     return fail(SW_ERR_SHAPE, "n_sink + n_window + 1 = %d exceeds %d", c.n_sink + c.n_window + 1, kMaxSlots);
   if (c.twin != 0 && c.twin != 1) return fail(SW_ERR_INVALID_ARG, "twin must be 0 or 1");
   if (c.sparse != 0 && c.sparse != 1) return fail(SW_ERR_INVALID_ARG, "sparse must be 0 or 1");
-  if (c.dtype != SW_BF16 && c.dtype != SW_F32) return fail(SW_ERR_INVALID_ARG, "unknown dtype %d", (int)c.dtype);
+  if (c.dtype != SW_BF16 && c.dtype != SW_F32 && c.dtype != SW_FP8)
+    return fail(SW_ERR_INVALID_ARG, "unknown dtype %d", (int)c.dtype);
   if (c.policy != SW_ROPE_S1_RELOCATE && c.policy != SW_ROPE_RELATIVE_TIME)
     return fail(SW_ERR_INVALID_ARG, "unknown RoPE policy %d", (int)c.policy);
   if (!(c.rope_theta > 1.0) || !std::isfinite(c.rope_theta))
     return fail(SW_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
   if (c.tile != kTile) return fail(SW_ERR_UNSUPPORTED, "tile must be %d", kTile);
+  if (c.dtype == SW_FP8 && c.head_dim != 128)
+    return fail(SW_ERR_UNSUPPORTED, "fp8 kernels are built for head_dim 128 (got %d)", c.head_dim);
+  if (c.dtype == SW_FP8 && (c.sparse || c.editing))
+    return fail(SW_ERR_UNSUPPORTED, "fp8 attention is built for the dense stream (no sparse, no editing)");
   if (c.dtype == SW_BF16 && c.head_dim != 128)
     return fail(SW_ERR_UNSUPPORTED, "bf16 kernels are built for head_dim 128 (got %d)", c.head_dim);
   if (c.dtype == SW_F32 && c.head_dim != 64 && c.head_dim != 128)
@@ -105,7 +110,7 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
     return fail(SW_ERR_SHAPE, "n_sink + n_window + 2 = %d exceeds %d with editing", c.n_sink + c.n_window + 2,
                 kMaxSlots);
   // the bf16 attention kernel re-rotates only the first 24 pairs per slot: time pairs must fit
-  if (c.dtype == SW_BF16 && (c.head_dim / 2) - 2 * ((c.head_dim / 2) / 3) > 24)
+  if (c.dtype != SW_F32 && (c.head_dim / 2) - 2 * ((c.head_dim / 2) / 3) > 24)
     return fail(SW_ERR_UNSUPPORTED, "time RoPE pairs exceed 24");
   const long long B = (long long)c.frames_per_block * c.lat_h * c.lat_w;
   if (B > 65536) return fail(SW_ERR_SHAPE, "block of %lld tokens exceeds 65536", B);
@@ -120,8 +125,9 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
   g.n_pad = g.nt * kTile;
   if ((long long)(c.n_sink + c.n_window + 1) * g.nt > kMaxKeyTiles && c.sparse)
     return fail(SW_ERR_SHAPE, "too many key tiles for the mask builder");
-  L->elem = c.dtype == SW_BF16 ? 2 : 4;
-  L->kv_bytes = align256((size_t)g.H * g.n_pad * g.d * L->elem);
+  L->elem = c.dtype == SW_BF16 ? 2 : (c.dtype == SW_FP8 ? 1 : 4);
+  // fp8: E4M3 values, then one E8M0 scale byte per 32 values
+  L->kv_bytes = align256((size_t)g.H * g.n_pad * g.d * L->elem + (c.dtype == SW_FP8 ? (size_t)g.H * g.n_pad * g.d / 32 : 0));
   L->pooled_bytes = c.sparse ? align256((size_t)g.H * g.nt * g.d * sizeof(float)) : 0;
   L->P = c.n_sink + c.n_window + 1;
   L->t_len = L->P * g.F;
@@ -130,7 +136,7 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
   L->pt = pairs - 2 * (pairs / 3);
   L->table_floats = 2 * ((size_t)L->t_len * L->pt + (size_t)g.lat_h * L->ph + (size_t)g.lat_w * L->pw);
   const int copies = c.twin ? 2 : 1;
-  L->ws_bytes = c.dtype == SW_BF16
+  L->ws_bytes = c.dtype != SW_F32
                     ? align256((size_t)kSplitRows * g.d * sizeof(float)) +
                           align256((size_t)kSplitRows * sizeof(float))
                     : 0;
@@ -254,7 +260,9 @@ sw_status write_block(sw_cache* c, const void* k, const void* v, char* kd, char*
   Geometry g = c->L.g;   // the slot keeps its capped stride (n_pad); the block fills its first rows
   g.B = tokens_of(c, frames);
   g.nt = (g.B + kTile - 1) / kTile;
-  const hipError_t e = launch_append(g, c->rt, c->cfg.dtype == SW_BF16, k, v, kd, vd, pd, c->stream);
+  const hipError_t e = c->cfg.dtype == SW_FP8
+                            ? launch_append_fp8(g, c->rt, k, v, kd, vd, c->stream)
+                            : launch_append(g, c->rt, c->cfg.dtype == SW_BF16, k, v, kd, vd, pd, c->stream);
   if (e != hipSuccess) return hip_fail(e, "append kernel launch");
   return SW_OK;
 }
@@ -576,6 +584,7 @@ sw_status sw_cache_append_qkv(sw_cache* c, const void* qkv_raw, const float* gam
   if (c->cfg.sparse && n_frames != c->cfg.frames_per_block)
     return fail(SW_ERR_UNSUPPORTED, "block-sparse caches hold full-length blocks only");
   if (c->cfg.head_dim != 128) return fail(SW_ERR_UNSUPPORTED, "the QKV epilogue is built for head_dim 128");
+  if (c->cfg.dtype == SW_FP8) return fail(SW_ERR_UNSUPPORTED, "the QKV epilogue writes bf16 or fp32 caches");
   st = check_stage(c, block_id, n_frames);
   if (st != SW_OK) return st;
   const int s = c->staging;
@@ -689,8 +698,10 @@ sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step, con
     slots[n_all++] = SlotPtrs{c->ks, c->vs, 0, tokens_of(c, c->staged_frames), 1};
   Geometry gq = c->L.g;   // the queries are the staged block's tokens
   gq.B = tokens_of(c, c->staged_frames);
-  const hipError_t e = launch_attend(gq, c->rt, c->cfg.dtype == SW_BF16, q_raw, slots, n_all, tile_idx, k_row,
-                                     out, lse_out, c->plan, c->stream);
+  const hipError_t e = c->cfg.dtype == SW_FP8
+                            ? launch_attend_fp8(gq, c->rt, q_raw, slots, n_all, out, lse_out, c->plan, c->stream)
+                            : launch_attend(gq, c->rt, c->cfg.dtype == SW_BF16, q_raw, slots, n_all, tile_idx, k_row,
+                                            out, lse_out, c->plan, c->stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return SW_OK;
 }
@@ -765,7 +776,10 @@ sw_status sw_cache_read_slot(sw_cache* c, int32_t logical_slot, sw_kv_kind kind,
   const bool noisy = kind == SW_KV_NOISY;
   Geometry g = c->L.g;
   g.B = tokens_of(c, frames);
-  hipError_t e = launch_unpack(g, c->cfg.dtype == SW_BF16, noisy ? c->kn[phys] : c->kc[phys],
+  hipError_t e = c->cfg.dtype == SW_FP8
+                    ? launch_unpack_fp8(g, noisy ? c->kn[phys] : c->kc[phys], noisy ? c->vn[phys] : c->vc[phys], k_out,
+                                        v_out, c->stream)
+                    : launch_unpack(g, c->cfg.dtype == SW_BF16, noisy ? c->kn[phys] : c->kc[phys],
                                noisy ? c->vn[phys] : c->vc[phys], k_out, v_out, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return hip_fail(e, "read-back");

@@ -65,6 +65,16 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
                          const SlotPtrs* slots, int n_slots, const int32_t* tile_idx, int k_row,
                          void* out, float* lse, const SplitPlan& plan, hipStream_t stream);
 
+// fp8 caches (d = 128): K1 quantising K (after block-local RoPE) and V to E4M3 with power-of-two
+// scales per 32 values (layout: append_fp8.hip); the fp8 attention (dense, bf16 queries and
+// output); the read-back, dequantised to fp32 [B][H][d].
+hipError_t launch_append_fp8(const Geometry& g, const RopeTab& rt, const void* k_raw, const void* v_raw, void* k_dst,
+                             void* v_dst, hipStream_t stream);
+hipError_t launch_attend_fp8(const Geometry& g, const RopeTab& rt, const void* q, const SlotPtrs* slots, int n_slots,
+                             void* out, float* lse, const SplitPlan& plan, hipStream_t stream);
+hipError_t launch_unpack_fp8(const Geometry& g, const void* k_src, const void* v_src, void* k_out, void* v_out,
+                             hipStream_t stream);
+
 // K4: block-sparse tile mask (bf16, d = 128).
 hipError_t launch_tile_mask(const Geometry& g, const RopeTab& rt, const void* q,
                             const float* const* pooled, const int* deltas, int n_slots,

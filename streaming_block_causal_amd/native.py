@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "swattn.h")
 SW_OK, SW_ERR_INVALID_ARG, SW_ERR_SHAPE, SW_ERR_STATE, SW_ERR_CAPACITY, SW_ERR_UNSUPPORTED, SW_ERR_HIP = range(7)
 STATUS_NAMES = ["SW_OK", "SW_ERR_INVALID_ARG", "SW_ERR_SHAPE", "SW_ERR_STATE", "SW_ERR_CAPACITY",
                 "SW_ERR_UNSUPPORTED", "SW_ERR_HIP"]
-SW_BF16, SW_F32 = 0, 1
+SW_BF16, SW_F32, SW_FP8 = 0, 1, 2
 SW_KV_CURRENT, SW_KV_CLEAN, SW_KV_NOISY, SW_KV_SOURCE = 0, 1, 2, 3
 SW_STEP_INTERMEDIATE, SW_STEP_FINAL = 0, 1
 SW_ROPE_S1_RELOCATE, SW_ROPE_RELATIVE_TIME = 0, 1
