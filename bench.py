@@ -377,7 +377,7 @@ def main():
         "latency_flatness": flat,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": load_traffic(args.workload),
-                     "kernel": ("attend_fp8_kernel<8>" if w.attn_fp8 else
+                     "kernel": ("attend_fp8_kernel<4>" if w.attn_fp8 else
                                 "attend_bf16_kernel<true, 4, false>" if w.sparse_keep else
                                 "attend_bf16_kernel<false, 8, true>" if w.editing else "attend_bf16_kernel<false, 8, false>"),
                      "flops_per_launch": flops_call},

@@ -733,7 +733,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_fp8_kernel(AttnArgs a) {
   constexpr int ROWS = 32 * NW;
   constexpr int NBUF = 2;
-  static_assert(NW == 8, "one 1 KB K chunk and one V^T chunk per wave and block");
+  static_assert(NW == 4 || NW == 8, "8 / NW one-KB chunks of K and of V^T per wave and block");
+  constexpr int NSTG = 8 / NW;
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[NBUF][KB * D];   // 8 KB
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[NBUF][D * KB];   // 8 KB
   __shared__ SlotPtrs sslot[kMaxSlots];
@@ -793,9 +794,15 @@ void attend_fp8_kernel(AttnArgs a) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) voff[u] = ln * 64 + 16 * ((2 * hf + u) ^ ((ln >> 2) & 3));
   // staging: wave w moves K rows 8w..8w+7 and V^T rows 16w..16w+15 of the block
-  const int kr = 8 * wave + (lane >> 3), vr = 16 * wave + (lane >> 2);
-  const int stk = kr * D + 16 * ((lane & 7) ^ (kr & 7));
-  const int stv = vr * n_pad + 16 * ((lane & 3) ^ ((vr >> 2) & 3));
+  // staging: chunk C = NW * p + wave moves K rows 8C..8C+7 and V^T rows 16C..16C+15 of the block
+  int stk[NSTG], stv[NSTG];
+#pragma unroll
+  for (int p = 0; p < NSTG; ++p) {
+    const int C = NW * p + wave;
+    const int kr = 8 * C + (lane >> 3), vr = 16 * C + (lane >> 2);
+    stk[p] = kr * D + 16 * ((lane & 7) ^ (kr & 7));
+    stv[p] = vr * n_pad + 16 * ((lane & 3) ^ ((vr >> 2) & 3));
+  }
   const size_t kstride = (size_t)n_pad * D;   // bytes per head, K and V^T alike
 
   // scales (E8M0 bytes) of a block: K -- the lane's key in tiles 0 and 1, shifted so that bytes 0
@@ -817,14 +824,18 @@ void attend_fp8_kernel(AttnArgs a) {
     const uint8_t* kg = reinterpret_cast<const uint8_t*>(
         uniform_ptr(static_cast<const uint8_t*>(sp.k) + h * kstride + (size_t)kb * KB * D));
     const uint8_t* vg = reinterpret_cast<const uint8_t*>(uniform_ptr(static_cast<const uint8_t*>(sp.v) + h * kstride + kb * KB));
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const __attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(kg + stk)),
-        reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&kbuf[buf][1024 * wave])),
-        16, 0, 0);
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const __attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(vg + stv)),
-        reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&vbuf[buf][1024 * wave])),
-        16, 0, 0);
+#pragma unroll
+    for (int p = 0; p < NSTG; ++p) {
+      const int C = NW * p + wave;
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const __attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(kg + stk[p])),
+          reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&kbuf[buf][1024 * C])),
+          16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const __attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(vg + stv[p])),
+          reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&vbuf[buf][1024 * C])),
+          16, 0, 0);
+    }
   };
 
   // ---- S^T = K Q^T for 64 keys: tiles t = 0, 1 (32 keys each), two channel chunks of 64
@@ -1032,6 +1043,11 @@ void attend_fp8_kernel(AttnArgs a) {
 
 constexpr int kDenseWaves = SWATTN_DENSE_WAVES;
 
+#ifndef SWATTN_FP8_WAVES
+#define SWATTN_FP8_WAVES 4
+#endif
+constexpr int kFp8Waves = SWATTN_FP8_WAVES;
+
 
 
 // Work split of a dense grid of `tiles` query tiles (`rows` queries each, `blocks` key blocks
@@ -1157,11 +1173,12 @@ hipError_t launch_attend_fp8(const Geometry& g, const RopeTab& rt, const void* q
   a.part_o = plan.part_o;
   a.part_lse = plan.part_lse;
   for (int i = 0; i < kMaxSlots; ++i) a.slot[i] = i < n_slots ? slots[i] : SlotPtrs{nullptr, nullptr, 0, 0, 0};
-  constexpr int NW = 8, ROWS = 32 * NW;
+  constexpr int NW = kFp8Waves, ROWS = 32 * NW;
   a.n_qt = (g.B + ROWS - 1) / ROWS;
   int blocks = 0;
   for (int l = 0; l < n_slots; ++l) blocks += (slots[l].count + KB - 1) / KB;
-  const int tail = plan_split(a, plan, a.n_qt * g.H, plan.cus, ROWS, blocks);
+  const int conc = NW == 4 ? 2 * plan.cus : plan.cus;   // workgroups resident at once
+  const int tail = plan_split(a, plan, a.n_qt * g.H, conc, ROWS, blocks);
   const int split = a.n_split;
   hipLaunchKernelGGL((attend_fp8_kernel<NW>), dim3(a.n_full + tail * split), dim3(64 * NW), 0, stream, a);
   if (split) hipLaunchKernelGGL((merge_kernel<ROWS>), dim3(tail, ROWS / kMergeRows), dim3(256), 0, stream, a);
