@@ -7,7 +7,9 @@
 // PixVerse R2 blog, section "Choice 3: bounded memory": RoPE relocation keeps
 // positions in the trained range) -- and stores K and V head-major so every
 // attention tile is one contiguous run of HBM.  bf16 V is stored transposed
-// (V^T [H][d][n_pad]) with keys permuted inside groups of 16 (perm16), the
+// and tile-major (V^T [H][n_pad / 128][d][128]: one 128-key tile of a head is one
+// contiguous 32 KB run, which also keeps the block-sparse kernel's scattered tile
+// reads inside few DRAM pages) with keys permuted inside groups of 16 (perm16), the
 // operand order of the attention kernel's P.V MFMA.  Pad rows are zero.  For
 // block-sparse caches it also writes the fp32 mean of the rotated K of every
 // 128-token tile (valid tokens only), the pooled keys the tile mask scores.
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
   if (BF16) {
     // V^T rows: dd = feature, 16 chunks of 8 keys (perm16 order) per 128-key tile
-    u16* vt = static_cast<u16*>(a.v_dst) + (size_t)h * D * a.n_pad + (size_t)j * kTile;
+    u16* vt = static_cast<u16*>(a.v_dst) + ((size_t)h * (a.n_pad / kTile) + j) * D * kTile;   // slot's full stride
     constexpr int VITEMS = D * 16 / 256;
 #pragma unroll 2
     for (int it = 0; it < VITEMS; ++it) {
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         const int k1 = 16 * g + perm16(8 * half + 2 * i + 1);
         w[i] = (uint32_t)vl[k0][dd] | ((uint32_t)vl[k1][dd] << 16);
       }
-      *reinterpret_cast<uint4*>(vt + (size_t)dd * a.n_pad + 8 * cc) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(vt + (size_t)dd * kTile + 8 * cc) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(const void* k_src, const vo
     if (BF16) {
       const int tile = r / kTile, in = r % kTile, g = in >> 4, c = perm16(in & 15);
       static_cast<T*>(v_out)[idx] = static_cast<const T*>(
-          v_src)[((size_t)h * D + dd) * n_pad + (size_t)tile * kTile + 16 * g + c];
+          v_src)[(((size_t)h * (n_pad / kTile) + tile) * D + dd) * kTile + 16 * g + c];
     } else {
       static_cast<T*>(v_out)[idx] = static_cast<const T*>(v_src)[((size_t)h * n_pad + r) * D + dd];
     }

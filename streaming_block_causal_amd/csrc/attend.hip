@@ -130,7 +130,7 @@ __device__ __forceinline__ bool block_at(const int32_t* list, int B, int n_slots
 //   V^T[128 dims][64 keys]: row d at d * 128 B, 16-byte chunk c at slot c ^ ((d >> 1) & 7)
 // A workgroup's NW waves each issue 16/NW K and 16/NW V loads (1 KB each) per block: load p of a
 // wave is K chunk NW * (p / 2) + wave for even p, the V^T chunk for odd p.  st[p] is the lane's
-// element offset inside the block (K: row-major, V^T: row stride n_pad).
+// element offset inside the block (K: row-major, V^T: row stride 128 inside its tile).
 __device__ __forceinline__ const u16* uniform_ptr(const void* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
@@ -251,7 +251,7 @@ void attend_bf16_kernel(AttnArgs a) {
       st[p] = r * D + 8 * ((lane & 15) ^ (r & 15));
     } else {
       const int d = 8 * C + (lane >> 3);
-      st[p] = d * n_pad + 8 * ((lane & 7) ^ ((d >> 1) & 7));
+      st[p] = d * kTile + 8 * ((lane & 7) ^ ((d >> 1) & 7));
     }
   }
 
@@ -267,7 +267,7 @@ void attend_bf16_kernel(AttnArgs a) {
     }
     const SlotPtrs sp = sslot[s];
     kb_ptr = uniform_ptr(static_cast<const u16*>(sp.k) + h * kstride + (size_t)kb * KB * D);
-    vb_ptr = uniform_ptr(static_cast<const u16*>(sp.v) + h * kstride + kb * KB);
+    vb_ptr = uniform_ptr(static_cast<const u16*>(sp.v) + h * kstride + (size_t)(kb >> 1) * D * kTile + (kb & 1) * KB);
   };
 
   // ---- S^T = K Q^T for 64 keys: two 32x32 tiles, lane holds 16 keys of query ln

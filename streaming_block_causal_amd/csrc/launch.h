@@ -28,7 +28,7 @@ struct Geometry {
 
 struct SlotPtrs {
   const void* k;   // rotated K, [H][n_pad][d]
-  const void* v;   // bf16: V^T [H][d][n_pad] (keys permuted in groups of 16); fp32: V [H][n_pad][d]
+  const void* v;   // bf16: V^T [H][n_pad/128][d][128] (keys permuted in groups of 16); fp32: V [H][n_pad][d]
   int delta;       // time base of the current block minus this slot's
   int count;       // tokens of the slot's block (<= n_pad)
   int aligned;     // 1: frame-aligned (editing source) -- key j is seen only by the queries of its
