@@ -110,8 +110,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int GPR = D / 8;              // 8-element groups per row
   constexpr int ITEMS = kTile * GPR / 256;
   constexpr int SUB = 256 / GPR;          // row sub-groups in the pooled reduction
-  __shared__ float red[SUB][D];
-  __shared__ __attribute__((aligned(16))) u16 vl[BF16 ? kTile : 1][D + 8];
+  constexpr int VROWS = kTile / 2;        // V rows staged in LDS at a time (bf16 transpose)
+  // one LDS buffer: first the pooled partial sums, then (bf16) half a tile of V rows; small
+  // enough for 8 workgroups per CU, so a whole 540p launch is resident at once
+  constexpr int SMEM = SUB * D * 4 > VROWS * (D + 8) * 2 ? SUB * D * 4 : VROWS * (D + 8) * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  float (*red)[D] = reinterpret_cast<float (*)[D]>(smem);
+  u16 (*vl)[D + 8] = reinterpret_cast<u16 (*)[D + 8]>(smem);
 
   const int tid = threadIdx.x, j = blockIdx.x, h = blockIdx.y;
   const int grp = tid % GPR;
@@ -155,13 +160,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     }
     Elem<BF16>::store8(kd + (size_t)r * D + grp * 8, x);
 
-    // V: raw row -> LDS (bf16, transposed below) or straight copy (fp32)
-    if (BF16) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < a.B) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(vr) +
-                                                       (size_t)r * a.row_stride + (size_t)h * D + grp * 8);
-      *reinterpret_cast<uint4*>(&vl[row][grp * 8]) = v;
-    } else {
+    if (!BF16) {   // fp32 V: a straight copy, head-major
       float y[8];
       if (r < a.B) {
         Elem<BF16>::load8(vr + (size_t)r * a.row_stride + (size_t)h * D + grp * 8, y);
@@ -177,34 +176,47 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   if (a.pooled) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[tid / GPR][grp * 8 + i] = pacc[i];
-  }
-  __syncthreads();
-
-  if (a.pooled && tid < D) {
-    float s = 0.f;
+    __syncthreads();
+    if (tid < D) {
+      float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < SUB; ++i) s += red[i][tid];
-    const int cnt = min(kTile, a.B - j * kTile);
-    a.pooled[((size_t)h * D + tid) * a.nt + j] = s / (float)cnt;   // [H][d][nt]: tiles contiguous
+      for (int i = 0; i < SUB; ++i) s += red[i][tid];
+      const int cnt = min(kTile, a.B - j * kTile);
+      a.pooled[((size_t)h * D + tid) * a.nt + j] = s / (float)cnt;   // [H][d][nt]: tiles contiguous
+    }
   }
 
   if (BF16) {
-    // V^T rows: dd = feature, 16 chunks of 8 keys (perm16 order) per 128-key tile
+    // V^T rows: dd = feature, 16 chunks of 8 keys (perm16 order) per 128-key tile, written in two
+    // halves of 64 keys through LDS
     u16* vt = static_cast<u16*>(a.v_dst) + ((size_t)h * (a.n_pad / kTile) + j) * D * kTile;   // slot's full stride
-    constexpr int VITEMS = D * 16 / 256;
-#pragma unroll 2
-    for (int it = 0; it < VITEMS; ++it) {
-      const int c = tid + 256 * it;
-      const int dd = c >> 4, cc = c & 15;
-      const int g = cc >> 1, half = cc & 1;
-      uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k0 = 16 * g + perm16(8 * half + 2 * i);
-        const int k1 = 16 * g + perm16(8 * half + 2 * i + 1);
-        w[i] = (uint32_t)vl[k0][dd] | ((uint32_t)vl[k1][dd] << 16);
+    for (int hv = 0; hv < 2; ++hv) {
+      __syncthreads();   // the buffer's previous use (pooled sums or the other half) is finished
+#pragma unroll
+      for (int it = 0; it < VROWS * GPR / 256; ++it) {
+        const int row = (tid + 256 * it) / GPR;
+        const int r = j * kTile + VROWS * hv + row;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < a.B) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(vr) +
+                                                         (size_t)r * a.row_stride + (size_t)h * D + grp * 8);
+        *reinterpret_cast<uint4*>(&vl[row][grp * 8]) = v;
       }
-      *reinterpret_cast<uint4*>(vt + (size_t)dd * kTile + 8 * cc) = make_uint4(w[0], w[1], w[2], w[3]);
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < D * 8 / 256; ++it) {
+        const int c = tid + 256 * it;
+        const int dd = c >> 3, cc = 8 * hv + (c & 7);
+        const int g = cc >> 1, half = cc & 1;
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k0 = 16 * g + perm16(8 * half + 2 * i) - VROWS * hv;
+          const int k1 = 16 * g + perm16(8 * half + 2 * i + 1) - VROWS * hv;
+          w[i] = (uint32_t)vl[k0][dd] | ((uint32_t)vl[k1][dd] << 16);
+        }
+        *reinterpret_cast<uint4*>(vt + (size_t)dd * kTile + 8 * cc) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
   }
 }
