@@ -8,7 +8,8 @@
 //     group); an element is the E4M3 rounding (to nearest, ties to even) of x / 2^e;
 //   * K [H][n_pad][128] bytes, groups = 32 consecutive channels of a key; its scale bytes
 //     (e + 127) follow all K data as [H][n_pad][4];
-//   * V^T [H][128][n_pad] bytes; inside each 64-key block, storage position 32 * s + j holds
+//   * V^T [H][n_pad / 64][128][64] bytes (block-major: one 64-key block of a head is one
+//     contiguous 8 KB run); inside each block, storage position 32 * s + j holds
 //     key 32 * (j / 16) + 8 * (j / 4 % 4) + 4 * s + j % 4 -- the order in which one lane of the
 //     attention kernel holds 32 probabilities of its query; the groups are the block's first
 //     and last 32 keys (positions [0, 16) + [32, 48) and [16, 32) + [48, 64)), per channel; the
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(Fp8Args a) {
 
   // V^T: (channel, 64-key block, group) items; group g (keys 32g..32g+31) sits at storage
   // positions [16g, 16g + 16) and [32 + 16g, 32 + 16g + 16)
-  uint8_t* vd = a.v_dst + (size_t)h * D * a.n_pad + (size_t)j * kTile;
+  uint8_t* vd = a.v_dst + ((size_t)h * (a.n_pad / 64) + 2 * j) * D * 64;   // block 2j of head h
   uint8_t* vsc = a.v_dst + (size_t)a.H * D * a.n_pad + (size_t)h * a.n_pad * 4;
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(Fp8Args a) {
     uint32_t w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = pack4_fp8(x[4 * i] * sc, x[4 * i + 1] * sc, x[4 * i + 2] * sc, x[4 * i + 3] * sc);
-    uint8_t* row = vd + (size_t)dd * a.n_pad + blk * 64;
+    uint8_t* row = vd + ((size_t)blk * D + dd) * 64;
     *reinterpret_cast<uint4*>(row + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
     *reinterpret_cast<uint4*>(row + 32 + 16 * g) = make_uint4(w[4], w[5], w[6], w[7]);
     const int gblk = j * 2 + blk;
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(256) void unpack_fp8_kernel(const uint8_t* k_src, c
     const int gblk = r >> 6, k = r & 63, half = (k >> 2) & 1, grp = k >> 5;
     const int jj = 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);    // inverse of v_key_of
     const int vbyte = vsc[((size_t)h * n_pad * 4) + ((size_t)(gblk * 2 + grp) * 32 + (dd & 31)) * 4 + (dd >> 5)];
-    v_out[idx] = fp8_decode(v_src[((size_t)h * D + dd) * n_pad + gblk * 64 + 32 * half + jj]) * pow2(vbyte);
+    v_out[idx] = fp8_decode(v_src[(((size_t)h * (n_pad / 64) + gblk) * D + dd) * 64 + 32 * half + jj]) * pow2(vbyte);
   }
 }
 

@@ -801,7 +801,7 @@ void attend_fp8_kernel(AttnArgs a) {
     const int C = NW * p + wave;
     const int kr = 8 * C + (lane >> 3), vr = 16 * C + (lane >> 2);
     stk[p] = kr * D + 16 * ((lane & 7) ^ (kr & 7));
-    stv[p] = vr * n_pad + 16 * ((lane & 3) ^ ((vr >> 2) & 3));
+    stv[p] = vr * KB + 16 * ((lane & 3) ^ ((vr >> 2) & 3));
   }
   const size_t kstride = (size_t)n_pad * D;   // bytes per head, K and V^T alike
 
@@ -823,7 +823,8 @@ void attend_fp8_kernel(AttnArgs a) {
     const SlotPtrs sp = sslot[s];
     const uint8_t* kg = reinterpret_cast<const uint8_t*>(
         uniform_ptr(static_cast<const uint8_t*>(sp.k) + h * kstride + (size_t)kb * KB * D));
-    const uint8_t* vg = reinterpret_cast<const uint8_t*>(uniform_ptr(static_cast<const uint8_t*>(sp.v) + h * kstride + kb * KB));
+    const uint8_t* vg = reinterpret_cast<const uint8_t*>(
+        uniform_ptr(static_cast<const uint8_t*>(sp.v) + h * kstride + (size_t)kb * D * KB));
 #pragma unroll
     for (int p = 0; p < NSTG; ++p) {
       const int C = NW * p + wave;

@@ -109,3 +109,26 @@ def test_fp8_540p_steady_state_two_heads():
     _say(f"[c8] {w.name}")
     _run(w, range(w.n_sink + w.n_window + 2), heads=[0, 17], rows=rows, steps=(w.n_steps,),
          check_from=w.n_sink + w.n_window)
+
+
+def test_fp8_variable_length_blocks():
+    """Blocks of 3, 1 and 2 frames (per-slot key counts, cumulative-frame relocation) in fp8."""
+    from streaming_block_causal_amd.cache import Cache
+    w = synth.tiny(8, name="fp8_varlen", lat_h=9, lat_w=13, n_heads=2, n_chunks=8, n_steps=1, policy="relative",
+                   frame_pattern=(3, 1, 2))
+    _say("[fp8 varlen]")
+    c = Cache(config_for(w), device="cuda")
+    st = ostream.Stream(w)
+    for n in range(w.n_chunks):
+        fn = synth.frames_of(w, n)
+        q, k, v = synth.qkv(w, n, 1)
+        c.append("current", to_dev(w, k), to_dev(w, v), n, n_frames=fn)
+        B = synth.block_shape(w, n)[0]
+        lse = torch.empty((w.n_heads, B), dtype=torch.float32, device="cuda")
+        out = c.attend(to_dev(w, q), "final", lse=lse)
+        torch.cuda.synchronize()
+        ref, rl, _ = st.call(n, 1)
+        ok, m = compare(to_f64(out), ref, "fp8", to_f64(lse), rl)
+        _say(f"  chunk {n} ({fn} frames): {m}")
+        assert ok, (n, m)
+        commit_block(c, w, n, n)

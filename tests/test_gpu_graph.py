@@ -24,14 +24,15 @@ def _commit(c, w, n):
     c.append("clean", None, None, n)
 
 
-@pytest.mark.parametrize("kind", ["dense", "twin", "sparse", "editing"])
+@pytest.mark.parametrize("kind", ["dense", "twin", "sparse", "editing", "fp8"])
 def test_graph_replay_equals_eager(kind):
     from streaming_block_causal_amd.cache import Cache
     kw = dict(lat_h=16, lat_w=20, n_heads=4, n_chunks=14, n_steps=2)
     w = {"dense": synth.tiny(2, name="g_dense", **kw),
          "twin": synth.tiny(3, name="g_twin", **kw),
          "sparse": synth.tiny(5, name="g_sparse", sparse_keep=0.3, **kw),
-         "editing": synth.tiny(7, name="g_edit", ref_frames=3, **kw)}[kind]
+         "editing": synth.tiny(7, name="g_edit", ref_frames=3, **kw),
+         "fp8": synth.tiny(8, name="g_fp8", **kw)}[kind]
     print(f"[graph {kind}]", flush=True)
     side = torch.cuda.Stream()
     eager = Cache(config_for(w), device="cuda")
