@@ -70,8 +70,6 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 // ------------------------------------------------------------------------------------
 constexpr int D = 128;
 constexpr int KB = 64;          // keys per LDS block
-constexpr int KS = D + 8;       // LDS row stride of K (bf16 elements)
-constexpr int VS = KB + 8;      // LDS row stride of V^T
 constexpr float kRescaleSlack = 8.0f;
 
 #ifndef QK_AHEAD

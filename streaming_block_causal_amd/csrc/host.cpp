@@ -404,11 +404,15 @@ sw_status sw_graph_end(sw_cache* c, sw_graph** out) {
   if (e != hipSuccess) return hip_fail(e, "end capture");
   hipGraphExec_t exec = nullptr;
   e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-  hipGraphDestroy(graph);
-  if (e != hipSuccess) return hip_fail(e, "graph instantiation");
+  const hipError_t ed = hipGraphDestroy(graph);   // the executable graph keeps its own copy
+  if (e == hipSuccess) e = ed;
+  if (e != hipSuccess) {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    return hip_fail(e, "graph instantiation");
+  }
   sw_graph* g = new (std::nothrow) sw_graph();
   if (!g) {
-    hipGraphExecDestroy(exec);
+    (void)hipGraphExecDestroy(exec);
     return fail(SW_ERR_CAPACITY, "host allocation failed");
   }
   g->exec = exec;
