@@ -73,7 +73,7 @@ constexpr int KB = 64;          // keys per LDS block
 constexpr float kRescaleSlack = 8.0f;
 
 #ifndef QK_AHEAD
-#define QK_AHEAD 2
+#define QK_AHEAD 1
 #endif
 #ifndef PV_AHEAD
 #define PV_AHEAD 8
