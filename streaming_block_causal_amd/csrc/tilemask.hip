@@ -12,13 +12,19 @@
 // pooled query turned by R_t(delta_l) -- the pooled keys come from the append
 // kernel, rotated at block-local positions.
 //
-// One workgroup per (query tile, head).  Reads the query tile once (HBM-bound,
-// a few microseconds at 540p) and the tiny pooled-key tables.
+// One workgroup per (query tile, head): it reads the query tile once and the small
+// pooled-key tables.  The selection is a per-wave radix search for the budget's
+// threshold score (32 ballot rounds): linear in the number of key tiles, where an
+// all-pairs rank is quadratic (4096 key tiles at the largest shapes).
 #include "device_common.h"
 
 namespace swattn {
 
 namespace {
+
+// query tiles per workgroup (one wave selects for each): 1 measured fastest at 540p, where
+// 4 (each pooled key read once for four tiles) leaves too few workgroups to hide latency
+constexpr int kQT = 1;
 
 struct MaskArgs {
   const u16* q;
@@ -32,23 +38,29 @@ struct MaskArgs {
   int delta[kMaxSlots];
 };
 
+// order-preserving map of a finite score to an unsigned key >= 1 (-0 and +0 map alike);
+// key 0 marks a tile that does not compete (forced, or past the end)
+__device__ __forceinline__ uint32_t score_key(float s) {
+  const uint32_t b = __float_as_uint(s + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   constexpr int D = 128;
-  // small LDS footprint (8 KB + the key-tile arrays sized at launch) so that many workgroups are
-  // resident and their latency-bound phases overlap: the partial sums of step 1 and the relocated
-  // queries of step 2 share one array
-  __shared__ float rq[16][D];
-  float (&red)[16][D] = rq;
-  float (&qs)[kMaxSlots][D] = rq;
-  extern __shared__ __attribute__((aligned(16))) float dyn[];   // sc[n_kv4], keep[n_kv4]
-  const int n_kv4 = (a.n_slots * a.nt + 3) & ~3;
-  float* sc = dyn;
-  unsigned char* keep = reinterpret_cast<unsigned char*>(dyn + n_kv4);
-
+  // dynamic LDS: first the partial sums of step 1 ([kQT][16][D] floats), then, reusing it, the
+  // relocated pooled queries ([kQT][n_slots][D] floats) and the score keys ([kQT][n_kv64])
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  __shared__ float2 xm[kQT][D / 2];
   __shared__ const float* spooled[kMaxSlots];
   __shared__ int sdelta[kMaxSlots];
-  const int tid = threadIdx.x, qt = blockIdx.x, h = blockIdx.y;
+
+  const int tid = threadIdx.x, qt0 = blockIdx.x * kQT, h = blockIdx.y;
+  const int n_qt = min(kQT, a.nt - qt0);
   const int n_kv = a.n_slots * a.nt;
+  const int n_kv64 = (n_kv + 63) & ~63;
+  float* red = dyn;
+  float* qs = dyn;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(dyn + kQT * a.n_slots * D);
   // the argument struct is never addressed (that would copy it to scratch): static indices only
 #pragma unroll
   for (int q = 0; q < kMaxSlots; ++q)
@@ -58,124 +70,158 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
     }
   const RopeTab rt = a.rt;
 
-  // 1. mean over the tile's valid queries of q rotated at block-local positions.  Thread t takes
-  //    4 pairs (16 bytes) of 8 rows; all loads are issued before any is used.
+  // 1. per query tile, the sum over its valid queries of q rotated at block-local positions.
+  //    Thread t takes 4 pairs (16 bytes) of 8 rows of every tile; all loads are issued first.
   {
     const int pg = tid & 15, rg = tid >> 4;   // pair group (4 pairs), row group
-    float acc8[8];
+    uint4 raw[kQT][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
-    uint4 raw[8];
-    int rows[8];
+    for (int t = 0; t < kQT; ++t)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      rows[i] = qt * kTile + rg + 16 * i;
-      raw[i] = rows[i] < a.B ? ldg16(a.q + ((size_t)rows[i] * a.H + h) * D + 8 * pg) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (rows[i] >= a.B) continue;
-      const int r = rows[i], f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
-      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float c, sn;
-        rope_cs(rt, 4 * pg + e, f, hh, ww, c, sn);
-        const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xffff0000u);
-        acc8[2 * e] += x0 * c - x1 * sn;
-        acc8[2 * e + 1] += x0 * sn + x1 * c;
+      for (int i = 0; i < 8; ++i) {
+        const int r = (qt0 + t) * kTile + rg + 16 * i;
+        raw[t][i] = (t < n_qt && r < a.B) ? ldg16(a.q + ((size_t)r * a.H + h) * D + 8 * pg) : make_uint4(0, 0, 0, 0);
       }
-    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[rg][8 * pg + e] = acc8[e];
+    for (int t = 0; t < kQT; ++t) {
+      float acc8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = (qt0 + t) * kTile + rg + 16 * i;
+        if (t >= n_qt || r >= a.B) continue;
+        const int f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
+        const uint32_t w[4] = {raw[t][i].x, raw[t][i].y, raw[t][i].z, raw[t][i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float c, sn;
+          rope_cs(rt, 4 * pg + e, f, hh, ww, c, sn);
+          const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xffff0000u);
+          acc8[2 * e] += x0 * c - x1 * sn;
+          acc8[2 * e + 1] += x0 * sn + x1 * c;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[(t * 16 + rg) * D + 8 * pg + e] = acc8[e];
+    }
   }
   __syncthreads();
-  // 2. relocate per slot: turn the time pairs by delta_l (the means are taken out of the shared
-  //    array before it is overwritten with the relocated queries)
-  const int p = tid;
-  float x0 = 0.f, x1 = 0.f;
-  if (tid < D / 2) {
-    const float cnt = (float)min(kTile, a.B - qt * kTile);
+  // 2. means (thread = (tile, pair)), then the relocation per slot: the time pairs are turned by
+  //    delta_l; the shared array is overwritten with the relocated queries only after the barrier
+  {
+    const int t = tid >> 6, p = tid & 63;
+    if (t < n_qt) {
+      const float cnt = (float)min(kTile, a.B - (qt0 + t) * kTile);
+      float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      x0 += red[g][2 * p];
-      x1 += red[g][2 * p + 1];
+      for (int g = 0; g < 16; ++g) {
+        x0 += red[(t * 16 + g) * D + 2 * p];
+        x1 += red[(t * 16 + g) * D + 2 * p + 1];
+      }
+      xm[t][p] = make_float2(x0 / cnt, x1 / cnt);
     }
-    x0 /= cnt;
-    x1 /= cnt;
   }
-  // each pair's mean is broadcast through LDS, then thread (slot, pair) rotates it: all table
-  // loads of the step are issued at once
-  __shared__ float2 xm[D / 2];
-  if (tid < D / 2) xm[tid] = make_float2(x0, x1);
   __syncthreads();
-  for (int idx = tid; idx < a.n_slots * (D / 2); idx += 256) {
-    const int sl = idx / (D / 2), pp = idx - sl * (D / 2);
+  for (int idx = tid; idx < n_qt * a.n_slots * (D / 2); idx += 256) {
+    const int pp = idx & (D / 2 - 1), ts = idx / (D / 2), sl = ts % a.n_slots, t = ts / a.n_slots;
     float c = 1.f, sn = 0.f;
     if (pp < rt.pt) {
       c = rt.cos_t[sdelta[sl] * rt.pt + pp];
       sn = rt.sin_t[sdelta[sl] * rt.pt + pp];
     }
-    const float2 m = xm[pp];
-    qs[sl][2 * pp] = m.x * c - m.y * sn;
-    qs[sl][2 * pp + 1] = m.x * sn + m.y * c;
+    const float2 m = xm[t][pp];
+    qs[(t * a.n_slots + sl) * D + 2 * pp] = m.x * c - m.y * sn;
+    qs[(t * a.n_slots + sl) * D + 2 * pp + 1] = m.x * sn + m.y * c;
   }
   __syncthreads();
-  // 3. scores of every key tile: lane per tile, the pooled keys are stored dimension-major so a
-  //    wave's loads of one dimension are contiguous.  Forced tiles get -inf: they are kept
-  //    anyway and must not take a rank from the others.
+  // 3. scores of every key tile against every query tile of the group: lane per key tile, the
+  //    pooled keys are stored dimension-major so a wave's loads of one dimension are contiguous,
+  //    and each pooled key is read once for the whole group.  Forced tiles (tile 0 of the first
+  //    sink, the query tile's own diagonal tile) do not compete: key 0.
   const int f_sink = a.has_sink ? 0 : -1;
-  const int f_diag = (a.n_slots - 1) * a.nt + qt;
-  for (int u = tid; u < n_kv4; u += 256) {
-    float sv = -INFINITY;
-    if (u < n_kv && u != f_sink && u != f_diag) {
+  const int f_diag0 = (a.n_slots - 1) * a.nt + qt0;
+  for (int u = tid; u < n_kv64; u += 256) {
+    float dot[kQT];
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) dot[t] = 0.f;
+    if (u < n_kv) {
       const int sl = u / a.nt, jt = u - sl * a.nt;
       const float* kp = spooled[sl] + (size_t)h * D * a.nt + jt;
-      float dot = 0.f;
-#pragma unroll 16
-      for (int i = 0; i < D; ++i) dot = fmaf(qs[sl][i], kp[(size_t)i * a.nt], dot);
-      sv = dot * a.inv_sqrt_d;
-    }
-    sc[u] = sv;
-  }
-  __syncthreads();
-  // 4. rank of every other tile: rank(u) = #tiles with a higher score, ties to the lower index;
-  //    tile u is kept when its rank is below the budget left after the forced tiles.  The scores
-  //    are read four at a time (LDS broadcast), no branch per comparison.
-  const int n_forced = 1 + (f_sink >= 0 ? 1 : 0);
-  const int free_budget = a.k_row - n_forced;
-  for (int u = tid; u < n_kv; u += 256) {
-    bool k = true;
-    if (u != f_sink && u != f_diag) {
-      const float su = sc[u];
-      int rank = 0;
-#pragma unroll 4
-      for (int v = 0; v < n_kv4; v += 4) {
-        const float4 s4 = *reinterpret_cast<const float4*>(&sc[v]);
-        rank += (s4.x > su || (s4.x == su && v < u)) ? 1 : 0;
-        rank += (s4.y > su || (s4.y == su && v + 1 < u)) ? 1 : 0;
-        rank += (s4.z > su || (s4.z == su && v + 2 < u)) ? 1 : 0;
-        rank += (s4.w > su || (s4.w == su && v + 3 < u)) ? 1 : 0;
+      const float* qp = qs + sl * D;
+#pragma unroll 32
+      for (int i = 0; i < D; ++i) {
+        const float kv = kp[(size_t)i * a.nt];
+#pragma unroll
+        for (int t = 0; t < kQT; ++t) dot[t] = fmaf(qp[t * a.n_slots * D + i], kv, dot[t]);
       }
-      k = rank < free_budget;
     }
-    keep[u] = k ? 1 : 0;
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) {
+      const bool cand = u < n_kv && u != f_sink && u != f_diag0 + t;
+      keys[t * n_kv64 + u] = cand ? score_key(dot[t] * a.inv_sqrt_d) : 0u;
+    }
   }
   __syncthreads();
-  // 5. ascending compaction by wave 0
-  if (tid < 64) {
-    int32_t* dst = a.out + ((size_t)h * a.nt + qt) * a.k_cap;
-    int count = 0;
-    for (int base = 0; base < n_kv; base += 64) {
-      const int u = base + tid;
-      const bool k = u < n_kv && keep[u];
-      const unsigned long long m = __ballot(k);
-      const int pos = count + __popcll(m & ((1ull << tid) - 1ull));
-      if (k && pos < a.k_cap) dst[pos] = u;
-      count += __popcll(m);
+  // 4. selection, one wave per query tile: the kept competitors are the `need` highest scores,
+  //    ties to the lower index.  T = the need-th highest key, found bit by bit from the top
+  //    (largest T with #(key >= T) >= need); then every key above T is kept and, of the keys
+  //    equal to T, the first need - #(key > T) in index order.
+  const int t = tid >> 6, lane = tid & 63;
+  if (t >= n_qt) return;
+  const uint32_t* kt = keys + t * n_kv64;
+  const int nch = n_kv64 >> 6;
+  uint32_t kr[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) kr[c] = c < nch ? kt[64 * c + lane] : 0u;
+  auto count_ge = [&](uint32_t K) {
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < nch) cnt += __popcll(__ballot(kr[c] >= K));
+    for (int c = 8; c < nch; ++c) cnt += __popcll(__ballot(kt[64 * c + lane] >= K));
+    return cnt;
+  };
+  const int n_forced = 1 + (f_sink >= 0 ? 1 : 0);
+  const int need = a.k_row - n_forced;
+  const int n_cand = count_ge(1u);
+  uint32_t T;
+  int take_eq;
+  if (need <= 0) {               // forced tiles only
+    T = 0xffffffffu;
+    take_eq = 0;
+  } else if (need >= n_cand) {   // every competitor
+    T = 0u;
+    take_eq = 0;
+  } else {
+    T = 0u;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = T | (1u << b);
+      if (count_ge(cand) >= need) T = cand;
     }
-    for (int pos = count + tid; pos < a.k_cap; pos += 64) dst[pos] = -1;
+    take_eq = need - (T == 0xffffffffu ? 0 : count_ge(T + 1u));
   }
+  // 5. ascending compaction of forced + kept tiles
+  int32_t* dst = a.out + ((size_t)h * a.nt + qt0 + t) * a.k_cap;
+  const int diag = f_diag0 + t;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int count = 0, eq_seen = 0;
+  auto emit = [&](int c, uint32_t k) {
+    const int u = 64 * c + lane;
+    const unsigned long long meq = __ballot(k != 0u && k == T);
+    const bool keep = u < n_kv && (u == f_sink || u == diag || (k != 0u && k > T) ||
+                                   (k != 0u && k == T && eq_seen + __popcll(meq & lt) < take_eq));
+    eq_seen += __popcll(meq);
+    const unsigned long long m = __ballot(keep);
+    const int pos = count + __popcll(m & lt);
+    if (keep && pos < a.k_cap) dst[pos] = u;
+    count += __popcll(m);
+  };
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    if (c < nch) emit(c, kr[c]);
+  for (int c = 8; c < nch; ++c) emit(c, kt[64 * c + lane]);
+  for (int pos = count + lane; pos < a.k_cap; pos += 64) dst[pos] = -1;
 }
 
 }  // namespace
@@ -203,9 +249,16 @@ hipError_t launch_tile_mask(const Geometry& g, const RopeTab& rt, const void* q,
     a.pooled[i] = i < n_slots ? pooled[i] : nullptr;
     a.delta[i] = i < n_slots ? deltas[i] : 0;
   }
-  const int n_kv4 = (n_slots * g.nt + 3) & ~3;
-  const size_t lds = (size_t)n_kv4 * sizeof(float) + (size_t)n_kv4;   // scores, keep flags
-  hipLaunchKernelGGL(tile_mask_kernel, dim3(g.nt, g.H), dim3(256), lds, stream, a);
+  const int n_kv64 = (n_slots * g.nt + 63) & ~63;
+  const size_t red = (size_t)kQT * 16 * g.d * sizeof(float);
+  const size_t sel = ((size_t)kQT * n_slots * g.d + (size_t)kQT * n_kv64) * sizeof(float);
+  const size_t lds = red > sel ? red : sel;   // <= 24 KB at the largest shapes
+  int dev = 0, lds_max = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      lds > (size_t)lds_max)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tile_mask_kernel, dim3((g.nt + kQT - 1) / kQT, g.H), dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 

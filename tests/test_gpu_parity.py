@@ -250,6 +250,45 @@ def test_c5_sparse_attention_with_oracle_mask():
     _check(w, to_f64(out)[:, heads][rows], to_f64(lse)[heads][:, rows], ref, rl, "sparse (oracle mask)")
 
 
+def test_tile_mask_many_key_tiles():
+    """640 key tiles per query tile (2 frames of 64 x 64 latents = 64 tiles a block; a sink, 8
+    window blocks and the current one): the selection walks a score table larger than the 512
+    entries a wave holds in registers."""
+    w = synth.tiny(5, name="mask_wide", frames=2, lat_h=64, lat_w=64, n_heads=2, n_sink=1, n_window=8,
+                   n_chunks=10, n_steps=1, sparse_keep=0.1)
+    assert (w.n_sink + w.n_window + 1) * otm.n_tiles(w.block_tokens) == 640
+    _run_sparse(w, 9, 1, heads=[0, 1])
+
+
+def test_tile_mask_ties_go_to_lower_index():
+    """All-zero queries score every key tile exactly 0 on both sides: the budget left after the
+    forced tiles goes to the lowest tile indices, bit for bit."""
+    w = synth.tiny(5, n_heads=2, lat_h=16, lat_w=20, n_chunks=4, n_steps=1, sparse_keep=0.3)
+    n = 3
+    c = _cache(w)
+    advance(c, w, n)
+    q, k, v = synth.qkv(w, n, 1)
+    qz = np.zeros_like(q)
+    c.append("current", to_dev(w, k), to_dev(w, v), n)
+    idx, k_row = c.build_tile_mask(to_dev(w, qz), w.sparse_keep)
+    torch.cuda.synchronize()
+    st = ostream.Stream(w)
+    qs, slots = st.slot_inputs(n, 1, current=(qz, k, v))
+    bases = st.bases(n)
+    roles = [r for r, _, _, _ in slots]
+    gpu = idx.cpu().numpy()
+    for h in range(w.n_heads):
+        q_rel = ostream.relocated_head(w, qs, h, bases[-1])
+        k_rel = [ostream.relocated_head(w, kk, h, bases[l]) for l, (_, _, kk, _) in enumerate(slots)]
+        kept, scores, budget = otm.build(q_rel, k_rel, roles, w.sparse_keep, w.tile)
+        assert k_row == budget and not np.any(scores[np.isfinite(scores)])
+        for i, ref in enumerate(kept):
+            assert list(gpu[h, i]) == list(ref), (h, i)
+            forced = {(len(slots) - 1) * otm.n_tiles(w.block_tokens) + i} | ({0} if roles[0] == "sink" else set())
+            rest = [u for u in ref if u not in forced]
+            assert rest == sorted(set(range(len(slots) * otm.n_tiles(w.block_tokens))) - forced)[:len(rest)]
+
+
 def test_sparse_mid_all_rows_and_keep_all():
     w = synth.tiny(5, n_heads=2, lat_h=16, lat_w=20, n_chunks=6, n_steps=1, sparse_keep=0.3)   # B = 960
     _say("[sparse mid]")
