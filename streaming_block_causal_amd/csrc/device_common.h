@@ -35,18 +35,16 @@ __device__ __forceinline__ u16 f2bf(float f) {
 // cos/sin of RoPE pair p for a token at (t, h, w).
 __device__ __forceinline__ void rope_cs(const RopeTab rt, int p, int t, int h, int w, float& c,
                                         float& s) {
+  CosSin v;
   if (p < rt.pt) {
-    c = rt.cos_t[t * rt.pt + p];
-    s = rt.sin_t[t * rt.pt + p];
+    v = rt.t[t * rt.pt + p];
   } else if (p < rt.pt + rt.ph) {
-    const int j = p - rt.pt;
-    c = rt.cos_h[h * rt.ph + j];
-    s = rt.sin_h[h * rt.ph + j];
+    v = rt.h[h * rt.ph + p - rt.pt];
   } else {
-    const int j = p - rt.pt - rt.ph;
-    c = rt.cos_w[w * rt.pw + j];
-    s = rt.sin_w[w * rt.pw + j];
+    v = rt.w[w * rt.pw + p - rt.pt - rt.ph];
   }
+  c = v.c;
+  s = v.s;
 }
 
 // Position of key c inside a 16-key group of the bf16 V^T cache layout.

@@ -222,10 +222,10 @@ void fill_tables(const Layout& L, double theta, std::vector<float>& t) {
   size_t o = 0;
   auto axis = [&](int n_pos, int n_pairs) {
     for (int pos = 0; pos < n_pos; ++pos)
-      for (int j = 0; j < n_pairs; ++j) {
+      for (int j = 0; j < n_pairs; ++j) {   // (cos, sin) side by side
         const double ang = (double)pos * std::pow(theta, -(double)j / (double)n_pairs);
-        t[o + (size_t)pos * n_pairs + j] = (float)std::cos(ang);
-        t[o + (size_t)n_pos * n_pairs + (size_t)pos * n_pairs + j] = (float)std::sin(ang);
+        t[o + 2 * ((size_t)pos * n_pairs + j)] = (float)std::cos(ang);
+        t[o + 2 * ((size_t)pos * n_pairs + j) + 1] = (float)std::sin(ang);
       }
     o += 2 * (size_t)n_pos * n_pairs;
   };
@@ -349,12 +349,9 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
       return hip_fail(e, "cache initialisation");
     }
     size_t o = 0;
-    c->rt.cos_t = tab + o; o += (size_t)L.t_len * L.pt;
-    c->rt.sin_t = tab + o; o += (size_t)L.t_len * L.pt;
-    c->rt.cos_h = tab + o; o += (size_t)L.g.lat_h * L.ph;
-    c->rt.sin_h = tab + o; o += (size_t)L.g.lat_h * L.ph;
-    c->rt.cos_w = tab + o; o += (size_t)L.g.lat_w * L.pw;
-    c->rt.sin_w = tab + o;
+    c->rt.t = reinterpret_cast<const CosSin*>(tab + o); o += 2 * (size_t)L.t_len * L.pt;
+    c->rt.h = reinterpret_cast<const CosSin*>(tab + o); o += 2 * (size_t)L.g.lat_h * L.ph;
+    c->rt.w = reinterpret_cast<const CosSin*>(tab + o);
   }
   c->rt.pt = L.pt;
   c->rt.ph = L.ph;

@@ -11,12 +11,17 @@ constexpr int kMaxSlots = 16;     // S + W + 1
 constexpr int kTile = 128;        // block-sparse tile edge, query-tile rows
 constexpr int kMaxKeyTiles = 4096;
 
-// fp32 cos/sin tables (computed on the host in fp64) for the three RoPE axes.
+// fp32 (cos, sin) of one RoPE angle, side by side so that one 8-byte load fetches both.
+struct __attribute__((aligned(8))) CosSin {
+  float c, s;
+};
+
+// cos/sin tables (computed on the host in fp64, stored fp32) for the three RoPE axes.
 // time: [t_len][pt], height: [lat_h][ph], width: [lat_w][pw].
 struct RopeTab {
-  const float* cos_t; const float* sin_t;
-  const float* cos_h; const float* sin_h;
-  const float* cos_w; const float* sin_w;
+  const CosSin* t;
+  const CosSin* h;
+  const CosSin* w;
   int pt, ph, pw, t_len;
 };
 

@@ -127,8 +127,9 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
     const int pp = idx & (D / 2 - 1), ts = idx / (D / 2), sl = ts % a.n_slots, t = ts / a.n_slots;
     float c = 1.f, sn = 0.f;
     if (pp < rt.pt) {
-      c = rt.cos_t[sdelta[sl] * rt.pt + pp];
-      sn = rt.sin_t[sdelta[sl] * rt.pt + pp];
+      const CosSin v = rt.t[sdelta[sl] * rt.pt + pp];
+      c = v.c;
+      sn = v.s;
     }
     const float2 m = xm[t][pp];
     qs[(t * a.n_slots + sl) * D + 2 * pp] = m.x * c - m.y * sn;
