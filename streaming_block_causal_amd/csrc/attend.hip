@@ -673,7 +673,10 @@ __device__ __forceinline__ int e8m0_of(float amax) {   // smallest e with amax /
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first conversion fills bytes 0-1 and the second bytes 2-3, so what the destination
+  // held before does not matter: passing the bits of `a` (dead afterwards) lets the compiler
+  // convert in place instead of first moving a zero into a fresh register
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
