@@ -102,7 +102,7 @@ typedef enum { SW_STEP_INTERMEDIATE = 0, SW_STEP_FINAL = 1 } sw_step_kind;
 typedef enum { SW_ROPE_S1_RELOCATE = 0, SW_ROPE_RELATIVE_TIME = 1 } sw_rope_policy;
 
 typedef struct {
-  int32_t n_heads;          /* H >= 1 */
+  int32_t n_heads;          /* 1 <= H <= 65535 */
   int32_t head_dim;         /* d: 128 (bf16 or fp32) or 64 (fp32) */
   int32_t frames_per_block; /* F >= 1; the cap when blocks carry their own frame count */
   int32_t lat_h, lat_w;     /* latent grid of a frame; B = F*lat_h*lat_w <= 65536 */
@@ -225,8 +225,10 @@ sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, float keep_frac,
  * in the cache dtype; lse_out (nullable) [H][B] fp32 natural-log sum of
  * exp(score) per query.  tile_idx == NULL: dense; otherwise block-sparse over
  * the key tiles listed in tile_idx [H][ceil(B/128)][k_row] (as written by
- * sw_build_tile_mask; indices must be valid, may be unsorted but are then
- * visited in the given order).  step selects the TwinCache copy. */
+ * sw_build_tile_mask; may be unsorted but are then visited in the given
+ * order; entries outside [0, n_key_tiles), such as the -1 padding a mask
+ * built with k_cap > budget carries, are skipped: pass k_row = k_cap for such
+ * a list).  step selects the TwinCache copy. */
 sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step,
                           const int32_t* tile_idx, int32_t k_row, void* out, float* lse_out);
 

@@ -84,8 +84,11 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
   if (c.n_heads < 1 || c.frames_per_block < 1 || c.lat_h < 1 || c.lat_w < 1)
     return fail(SW_ERR_INVALID_ARG, "n_heads, frames_per_block, lat_h, lat_w must be >= 1");
   if (c.n_sink < 0 || c.n_window < 0) return fail(SW_ERR_INVALID_ARG, "n_sink, n_window must be >= 0");
-  if (c.n_sink + c.n_window + 1 > kMaxSlots)
-    return fail(SW_ERR_SHAPE, "n_sink + n_window + 1 = %d exceeds %d", c.n_sink + c.n_window + 1, kMaxSlots);
+  if (c.n_heads > 65535) return fail(SW_ERR_SHAPE, "n_heads %d exceeds 65535 (a launch grid dimension)", c.n_heads);
+  // 64-bit sums: n_sink and n_window are caller-controlled int32
+  if ((long long)c.n_sink + c.n_window + 1 > kMaxSlots)
+    return fail(SW_ERR_SHAPE, "n_sink + n_window + 1 = %lld exceeds %d", (long long)c.n_sink + c.n_window + 1,
+                kMaxSlots);
   if (c.twin != 0 && c.twin != 1) return fail(SW_ERR_INVALID_ARG, "twin must be 0 or 1");
   if (c.sparse != 0 && c.sparse != 1) return fail(SW_ERR_INVALID_ARG, "sparse must be 0 or 1");
   if (c.dtype != SW_BF16 && c.dtype != SW_F32 && c.dtype != SW_FP8)
@@ -106,7 +109,7 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
   if (c.sparse && c.dtype != SW_BF16) return fail(SW_ERR_UNSUPPORTED, "block-sparse needs bf16");
   if (c.editing != 0 && c.editing != 1) return fail(SW_ERR_INVALID_ARG, "editing must be 0 or 1");
   if (c.editing && c.sparse) return fail(SW_ERR_UNSUPPORTED, "frame-aligned editing attention is dense only");
-  if (c.editing && c.n_sink + c.n_window + 2 > kMaxSlots)
+  if (c.editing && (long long)c.n_sink + c.n_window + 2 > kMaxSlots)
     return fail(SW_ERR_SHAPE, "n_sink + n_window + 2 = %d exceeds %d with editing", c.n_sink + c.n_window + 2,
                 kMaxSlots);
   // the bf16 attention kernel re-rotates only the first 24 pairs per slot: time pairs must fit

@@ -143,9 +143,11 @@ def test_error_paths_leave_state_unchanged():
 def test_config_validation():
     base = config_for(synth.WORKLOADS[2])
     bad = [dict(head_dim=64), dict(n_sink=10, n_window=6), dict(tile=64), dict(n_heads=0),
-           dict(rope_theta=0.5), dict(lat_h=300, lat_w=300)]
+           dict(rope_theta=0.5), dict(lat_h=300, lat_w=300), dict(n_sink=1, n_window=2**31 - 1),
+           dict(n_heads=65536)]
     codes = [native.SW_ERR_UNSUPPORTED, native.SW_ERR_SHAPE, native.SW_ERR_UNSUPPORTED,
-             native.SW_ERR_INVALID_ARG, native.SW_ERR_INVALID_ARG, native.SW_ERR_SHAPE]
+             native.SW_ERR_INVALID_ARG, native.SW_ERR_INVALID_ARG, native.SW_ERR_SHAPE, native.SW_ERR_SHAPE,
+             native.SW_ERR_SHAPE]
     import dataclasses
     for kw, code in zip(bad, codes):
         with pytest.raises(native.SwError) as e:
