@@ -107,8 +107,10 @@ def test_bf16_mid_stream_all_rows():
 
 
 def test_bf16_odd_shapes():
+    # includes the caches without a window: sinks + current only, and the current block alone
     for kw in (dict(lat_h=1, lat_w=1, frames=1), dict(lat_h=3, lat_w=43, frames=1), dict(lat_h=16, lat_w=16, frames=2),
-               dict(lat_h=7, lat_w=9, frames=3, n_sink=2, n_window=2)):
+               dict(lat_h=7, lat_w=9, frames=3, n_sink=2, n_window=2), dict(lat_h=8, lat_w=20, frames=1, n_sink=2, n_window=0),
+               dict(lat_h=8, lat_w=20, frames=1, n_sink=0, n_window=0)):
         w = synth.tiny(2, **{**dict(n_heads=2, n_chunks=5, n_steps=1), **kw})
         _say(f"[bf16 shape] {kw} B={w.block_tokens}")
         c = _cache(w)
