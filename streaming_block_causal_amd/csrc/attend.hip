@@ -113,7 +113,11 @@ __device__ __forceinline__ void load_q(const RopeTab rt, const u16* qp, bool val
 // a short last tile, or an invalid tile index).
 __device__ __forceinline__ bool block_at(const int32_t* list, int B, int n_slots, int nt, int nkb, int i, int& sl,
                                          int& kb, int& kvalid) {
-  const int tix = list[i >> 1];
+  // the list is read-only during the launch and its address is uniform: a scalar (constant
+  // address space) load, counted on lgkmcnt.  A vector load here would be waited for with
+  // vmcnt(0), which also waits for the staging loads of the next block issued just before.
+  const int tix = *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(list + (i >> 1)));
   if (tix < 0 || tix >= n_slots * nt) return false;   // never read outside the cache
   sl = tix / nt;
   kb = 2 * (tix - sl * nt) + (i & 1);
