@@ -32,17 +32,16 @@ __device__ __forceinline__ u16 f2bf(float f) {
   return __builtin_bit_cast(u16, h);
 }
 
-// cos/sin of RoPE pair p for a token at (t, h, w).
+// cos/sin of RoPE pair p for a token at (t, h, w).  Branch-free: the table and the index are
+// selected and one load is issued, so the loads of several pairs can be in flight together
+// (lanes of one wave often hold pairs of different axes; with a branch per axis every branch's
+// load would be issued and waited for on its own).
 __device__ __forceinline__ void rope_cs(const RopeTab rt, int p, int t, int h, int w, float& c,
                                         float& s) {
-  CosSin v;
-  if (p < rt.pt) {
-    v = rt.t[t * rt.pt + p];
-  } else if (p < rt.pt + rt.ph) {
-    v = rt.h[h * rt.ph + p - rt.pt];
-  } else {
-    v = rt.w[w * rt.pw + p - rt.pt - rt.ph];
-  }
+  const bool on_t = p < rt.pt, on_h = p < rt.pt + rt.ph;
+  const CosSin* tab = on_t ? rt.t : (on_h ? rt.h : rt.w);
+  const int idx = on_t ? t * rt.pt + p : (on_h ? h * rt.ph + (p - rt.pt) : w * rt.pw + (p - rt.pt - rt.ph));
+  const CosSin v = tab[idx];
   c = v.c;
   s = v.s;
 }
