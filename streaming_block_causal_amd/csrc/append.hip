@@ -129,45 +129,42 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) pacc[i] = 0.f;
 
+  // Loads are unconditional (a pad row reads row 0, always valid, and its values are replaced
+  // by zeros), so the compiler can keep the loads of several rows in flight: behind a branch
+  // each load was issued and waited for on its own.
 #pragma unroll 2
   for (int it = 0; it < ITEMS; ++it) {
     const int row = (tid + 256 * it) / GPR;
     const int r = j * kTile + row;
+    const bool ok = r < a.B;
+    const int rc = ok ? r : 0;
     float x[8];
-    if (NORM && r < a.B) {   // q: normalise, store token-major (the attention call rotates it)
+    if (NORM) {   // q: normalise, store token-major (the attention call rotates it)
       float y[8];
-      Elem<BF16>::load8(static_cast<const T*>(a.q_raw) + (size_t)r * a.row_stride + (size_t)h * D + grp * 8, y);
+      Elem<BF16>::load8(static_cast<const T*>(a.q_raw) + (size_t)rc * a.row_stride + (size_t)h * D + grp * 8, y);
       rms_scale8(y, a.gq, grp * 8, D, a.eps);
-      Elem<BF16>::store8(static_cast<T*>(a.q_out) + ((size_t)r * a.H + h) * D + grp * 8, y);
+      if (ok) Elem<BF16>::store8(static_cast<T*>(a.q_out) + ((size_t)r * a.H + h) * D + grp * 8, y);
     }
-    if (r < a.B) {
-      Elem<BF16>::load8(kr + (size_t)r * a.row_stride + (size_t)h * D + grp * 8, x);
-      if (NORM) rms_scale8(x, a.gk, grp * 8, D, a.eps);
-      const int f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
+    Elem<BF16>::load8(kr + (size_t)rc * a.row_stride + (size_t)h * D + grp * 8, x);
+    if (NORM) rms_scale8(x, a.gk, grp * 8, D, a.eps);
+    const int f = rc / a.hw, rem = rc - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float c, s;
-        rope_cs(rt, grp * 4 + i, f, hh, ww, c, s);
-        const float x0 = x[2 * i], x1 = x[2 * i + 1];
-        x[2 * i] = x0 * c - x1 * s;
-        x[2 * i + 1] = x0 * s + x1 * c;
-        pacc[2 * i] += x[2 * i];
-        pacc[2 * i + 1] += x[2 * i + 1];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      float c, s;
+      rope_cs(rt, grp * 4 + i, f, hh, ww, c, s);
+      const float x0 = x[2 * i], x1 = x[2 * i + 1];
+      x[2 * i] = ok ? x0 * c - x1 * s : 0.f;
+      x[2 * i + 1] = ok ? x0 * s + x1 * c : 0.f;
+      pacc[2 * i] += x[2 * i];
+      pacc[2 * i + 1] += x[2 * i + 1];
     }
     Elem<BF16>::store8(kd + (size_t)r * D + grp * 8, x);
 
     if (!BF16) {   // fp32 V: a straight copy, head-major
       float y[8];
-      if (r < a.B) {
-        Elem<BF16>::load8(vr + (size_t)r * a.row_stride + (size_t)h * D + grp * 8, y);
-      } else {
+      Elem<BF16>::load8(vr + (size_t)rc * a.row_stride + (size_t)h * D + grp * 8, y);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = 0.f;
-      }
+      for (int i = 0; i < 8; ++i) y[i] = ok ? y[i] : 0.f;
       T* vd = static_cast<T*>(a.v_dst) + ((size_t)h * a.n_pad + r) * D + grp * 8;
       Elem<BF16>::store8(vd, y);
     }
@@ -193,14 +190,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
     for (int hv = 0; hv < 2; ++hv) {
       __syncthreads();   // the buffer's previous use (pooled sums or the other half) is finished
+      constexpr int NV = VROWS * GPR / 256;
+      uint4 v[NV];
 #pragma unroll
-      for (int it = 0; it < VROWS * GPR / 256; ++it) {
+      for (int it = 0; it < NV; ++it) {   // all loads first (unconditional, see above)
+        const int r = j * kTile + VROWS * hv + (tid + 256 * it) / GPR;
+        v[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(vr) + (size_t)(r < a.B ? r : 0) * a.row_stride +
+                                                (size_t)h * D + grp * 8);
+      }
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
         const int row = (tid + 256 * it) / GPR;
-        const int r = j * kTile + VROWS * hv + row;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < a.B) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(vr) +
-                                                         (size_t)r * a.row_stride + (size_t)h * D + grp * 8);
-        *reinterpret_cast<uint4*>(&vl[row][grp * 8]) = v;
+        const bool ok = j * kTile + VROWS * hv + row < a.B;
+        *reinterpret_cast<uint4*>(&vl[row][grp * 8]) = ok ? v[it] : make_uint4(0, 0, 0, 0);
       }
       __syncthreads();
 #pragma unroll
