@@ -61,26 +61,26 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(Fp8Args a) {
   uint8_t* kd = a.k_dst + (size_t)h * a.n_pad * D;
   uint8_t* ksc = a.k_dst + (size_t)a.H * a.n_pad * D + (size_t)h * a.n_pad * 4;
 
+  // loads are unconditional (a pad row reads row 0, always valid, and is zeroed by select), so a
+  // row's K, V and table loads are in flight together instead of one branch at a time
 #pragma unroll 2
   for (int it = 0; it < kTile * GPR / 256; ++it) {
     const int row = (tid + 256 * it) / GPR;
     const int r = j * kTile + row;
+    const bool ok = r < a.B;
+    const int rc = ok ? r : 0;
+    const uint4 raw = ldg16(a.k_raw + ((size_t)rc * a.H + h) * D + grp * 8);
+    const uint4 v = ldg16(a.v_raw + ((size_t)rc * a.H + h) * D + grp * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const int f = rc / a.hw, rem = rc - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
     float x[8];
-    if (r < a.B) {
-      const uint4 raw = ldg16(a.k_raw + ((size_t)r * a.H + h) * D + grp * 8);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-      const int f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float c, s;
-        rope_cs(rt, grp * 4 + i, f, hh, ww, c, s);
-        const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xffff0000u);
-        x[2 * i] = x0 * c - x1 * s;
-        x[2 * i + 1] = x0 * s + x1 * c;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      float c, s;
+      rope_cs(rt, grp * 4 + i, f, hh, ww, c, s);
+      const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xffff0000u);
+      x[2 * i] = ok ? x0 * c - x1 * s : 0.f;
+      x[2 * i + 1] = ok ? x0 * s + x1 * c : 0.f;
     }
     // group of 32 channels = 4 neighbouring lanes of the row
     float amax = 0.f;
@@ -95,10 +95,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(Fp8Args a) {
     q.y = pack4_fp8(x[4] * sc, x[5] * sc, x[6] * sc, x[7] * sc);
     *reinterpret_cast<uint2*>(kd + (size_t)r * D + grp * 8) = q;
     if ((grp & 3) == 0) ksc[(size_t)r * 4 + (grp >> 2)] = (uint8_t)(e + 127);
-
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < a.B) v = ldg16(a.v_raw + ((size_t)r * a.H + h) * D + grp * 8);
-    *reinterpret_cast<uint4*>(&vl[row][grp * 8]) = v;
+    *reinterpret_cast<uint4*>(&vl[row][grp * 8]) = ok ? v : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
