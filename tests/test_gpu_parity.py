@@ -291,6 +291,27 @@ def test_tile_mask_ties_go_to_lower_index():
             assert rest == sorted(set(range(len(slots) * otm.n_tiles(w.block_tokens))) - forced)[:len(rest)]
 
 
+def test_tile_list_padding_is_skipped():
+    """A mask built with k_cap above the budget carries -1 padding after the kept tiles; passed
+    with k_row = k_cap, the attention skips the padding and equals the unpadded call bit for bit."""
+    w = synth.tiny(5, n_heads=2, lat_h=16, lat_w=20, n_chunks=4, n_steps=1, sparse_keep=0.3)
+    n = 3
+    c = _cache(w)
+    advance(c, w, n)
+    q, k, v = synth.qkv(w, n, 1)
+    c.append("current", to_dev(w, k), to_dev(w, v), n)
+    qd = to_dev(w, q)
+    idx, k_row = c.build_tile_mask(qd, w.sparse_keep)
+    wide, k_row2 = c.build_tile_mask(qd, w.sparse_keep, k_cap=k_row + 3)
+    torch.cuda.synchronize()
+    assert k_row2 == k_row
+    assert torch.equal(wide[:, :, :k_row], idx) and bool((wide[:, :, k_row:] == -1).all())
+    o1 = c.attend(qd, "final", tile_idx=idx, k_row=k_row)
+    o2 = c.attend(qd, "final", tile_idx=wide, k_row=k_row + 3)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
 def test_sparse_mid_all_rows_and_keep_all():
     w = synth.tiny(5, n_heads=2, lat_h=16, lat_w=20, n_chunks=6, n_steps=1, sparse_keep=0.3)   # B = 960
     _say("[sparse mid]")
