@@ -15,8 +15,9 @@
 // bf16) each time the key loop enters a new slot; stored keys are never touched
 // again, which also makes the result independent of where the ring sits.
 //
-// bf16 path (d = 128): one workgroup = 4 waves = 128 queries of one head; each
-// wave owns 32 queries.  Keys stream through LDS 64 at a time.  A wave computes
+// bf16 path (d = 128): one workgroup = 8 waves = 256 queries of one head (dense; the
+// block-sparse launch uses 4 waves = 128 queries, two workgroups per CU); each wave
+// owns 32 queries.  Keys stream through LDS 64 at a time.  A wave computes
 // the transposed score tile S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so every
 // lane holds 16 keys of ONE query: the softmax row max and sum are in-register
 // plus one cross-half exchange (v_permlane32_swap).  P^T stays in registers as
@@ -24,6 +25,11 @@
 // of 16) makes the matching A operand one 16-byte LDS read.  Online softmax runs
 // in the log2 domain with the 1/sqrt(d) scale folded into one FMA before v_exp.
 // Block-sparse (K3): the same loop, over the listed 128-key tiles only.
+//
+// fp8 path (d = 128, E4M3 cache with power-of-two scales per 32 values): the same
+// structure with v_mfma_scale_f32_32x32x64_f8f6f4 (64-deep contractions, the scale
+// bytes applied by the instruction); the probabilities are rounded to E4M3 and
+// their row sums come from one more scaled MFMA with an all-ones operand.
 //
 // fp32 path (d = 64 or 128): one thread per query, keys broadcast from LDS;
 // exact-ish reference-grade arithmetic for the small fp32 workload.
@@ -70,14 +76,14 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 // ------------------------------------------------------------------------------------
 constexpr int D = 128;
 constexpr int KB = 64;          // keys per LDS block
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kRescaleSlack = 8.0f;   // log2 units: exp2 arguments stay <= 8 between rescales
 
 #ifndef QK_AHEAD
-#define QK_AHEAD 1
+#define QK_AHEAD 1   // K operands read this many MFMA pairs ahead
 #endif
 #ifndef PV_AHEAD
-#define PV_AHEAD 8
-#endif   // log2 units: exp2 arguments stay <= 8 between rescales
+#define PV_AHEAD 8   // V^T operands of the P.V MFMAs read before the softmax
+#endif
 
 // Q^T operand of one wave: lane (hf, ln) holds q[row][16j + 8hf + 0..7] for j in [J0, J1), rotated
 // at time frame + delta (fp32 math, bf16 result).  Rows past the block give a zero operand.
