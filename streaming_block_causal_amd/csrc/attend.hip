@@ -56,8 +56,8 @@ struct AttnArgs {
   int n_qt;           // query tiles per head of this launch
   int n_full;         // workgroups that own a whole query tile
   int n_split;        // key-range pieces of each remaining tile (0: none)
-  float* part_o;      // [piece][128][128] normalised partial outputs of split tiles
-  float* part_lse;    // [piece][128] their log2 sum-exp
+  float* part_o;      // [piece][rows of a tile][d] normalised partial outputs of split tiles
+  float* part_lse;    // [piece][rows of a tile] their log2 sum-exp
   RopeTab rt;
   SlotPtrs slot[kMaxSlots];
 };
