@@ -31,8 +31,9 @@
 // bytes applied by the instruction); the probabilities are rounded to E4M3 and
 // their row sums come from one more scaled MFMA with an all-ones operand.
 //
-// fp32 path (d = 64 or 128): one thread per query, keys broadcast from LDS;
-// exact-ish reference-grade arithmetic for the small fp32 workload.
+// fp32 path (d = 64 or 128): four lanes per query (a quarter of the dimensions each,
+// scores reduced with two lane exchanges), keys broadcast from LDS; plain fp32
+// arithmetic for the small fp32 workload.
 #include <algorithm>
 
 #include "device_common.h"
@@ -564,36 +565,38 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 // fp32 kernel: one thread per query, keys broadcast from LDS, 16-key sub-blocks
 // ------------------------------------------------------------------------------------
 template <int DD>
-__global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
-  constexpr int KBF = 32;
+__global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs a) {
+  // 64 queries per workgroup, 4 lanes per query: lane `sub` owns dims [sub * DW, (sub + 1) * DW)
+  // of the rotated query and of the accumulator; scores are reduced over the 4 lanes
+  constexpr int KBF = 32, LPQ = 4, DW = DD / LPQ;
   __shared__ float kl[KBF][DD];
   __shared__ float vl[KBF][DD];
   __shared__ SlotPtrs sslot[kMaxSlots];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, sub = tid & (LPQ - 1);
 #pragma unroll
   for (int q = 0; q < kMaxSlots; ++q)
     if (tid == q) sslot[q] = a.slot[q];
   const RopeTab rt = a.rt;
   __syncthreads();
   const int h = blockIdx.y;
-  const int qrow = blockIdx.x * 64 + tid;
+  const int qrow = blockIdx.x * 64 + tid / LPQ;
   const bool qvalid = qrow < a.B;
   const int qf = qrow / a.hw, qrem = qrow - qf * a.hw;
   const int qh = qrem / a.lat_w, qw = qrem - qh * a.lat_w;
-  const float* qp = static_cast<const float*>(a.q) + ((size_t)qrow * a.H + h) * DD;
-  float qr[DD], acc[DD];
+  const float* qp = static_cast<const float*>(a.q) + ((size_t)qrow * a.H + h) * DD + sub * DW;
+  float qr[DW], acc[DW];
 #pragma unroll
-  for (int i = 0; i < DD; ++i) acc[i] = 0.f;
+  for (int i = 0; i < DW; ++i) acc[i] = 0.f;
   float m_run = -3.0e38f, l_run = 0.f;   // finite floor: a fully masked sub-block gives alpha = 1
   const float scale = a.scale_log2;
 
   for (int sl = 0; sl < a.n_slots; ++sl) {
     const int t = qf + sslot[sl].delta;
 #pragma unroll
-    for (int p = 0; p < DD / 2; ++p) {
+    for (int p = 0; p < DW / 2; ++p) {
       float c = 1.f, s = 0.f, x0 = 0.f, x1 = 0.f;
       if (qvalid) {
-        rope_cs(rt, p, t, qh, qw, c, s);
+        rope_cs(rt, sub * (DW / 2) + p, t, qh, qw, c, s);
         x0 = qp[2 * p];
         x1 = qp[2 * p + 1];
       }
@@ -611,7 +614,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
     const int k_hi = al ? min(count, (r_last / a.hw + 1) * a.hw) : count;
     for (int k0 = k_lo; k0 < k_hi; k0 += KBF) {
       __syncthreads();
-      for (int i = tid; i < KBF * DD; i += 64) {
+      for (int i = tid; i < KBF * DD; i += 256) {
         kl[i / DD][i % DD] = kbase[(size_t)k0 * DD + i];
         vl[i / DD][i % DD] = vbase[(size_t)k0 * DD + i];
       }
@@ -623,7 +626,9 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
       for (int j = 0; j < KBF; ++j) {
         float dot = 0.f;
 #pragma unroll
-        for (int i = 0; i < DD; ++i) dot = fmaf(qr[i], kl[j][i], dot);
+        for (int i = 0; i < DW; ++i) dot = fmaf(qr[i], kl[j][sub * DW + i], dot);
+        dot += __shfl_xor(dot, 1);
+        dot += __shfl_xor(dot, 2);
         const bool seen = j < nk && (!al || (k0 + j) / a.hw == qf);
         sc[j] = seen ? dot * scale : -INFINITY;
         mx = fmaxf(mx, sc[j]);
@@ -633,22 +638,22 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < DD; ++i) acc[i] *= alpha;
+      for (int i = 0; i < DW; ++i) acc[i] *= alpha;
 #pragma unroll
       for (int j = 0; j < KBF; ++j) {
         const float p = __builtin_amdgcn_exp2f(sc[j] - m_new);
         l_run += p;
 #pragma unroll
-        for (int i = 0; i < DD; ++i) acc[i] = fmaf(p, vl[j][i], acc[i]);
+        for (int i = 0; i < DW; ++i) acc[i] = fmaf(p, vl[j][sub * DW + i], acc[i]);
       }
     }
   }
   if (qvalid) {
-    float* op = static_cast<float*>(a.o) + ((size_t)qrow * a.H + h) * DD;
+    float* op = static_cast<float*>(a.o) + ((size_t)qrow * a.H + h) * DD + sub * DW;
     const float inv = 1.f / l_run;
 #pragma unroll
-    for (int i = 0; i < DD; ++i) op[i] = acc[i] * inv;
-    if (a.lse) a.lse[(size_t)h * a.B + qrow] = (m_run + __log2f(l_run)) * kLn2;
+    for (int i = 0; i < DW; ++i) op[i] = acc[i] * inv;
+    if (a.lse && sub == 0) a.lse[(size_t)h * a.B + qrow] = (m_run + __log2f(l_run)) * kLn2;
   }
 }
 
@@ -1150,7 +1155,7 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
     if (split) hipLaunchKernelGGL((merge_kernel<ROWS>), dim3(tail, ROWS / kMergeRows), dim3(256), 0, stream, a);
   } else {
     if (tile_idx) return hipErrorInvalidValue;
-    const dim3 grid((g.B + 63) / 64, g.H), block(64);
+    const dim3 grid((g.B + 63) / 64, g.H), block(256);
     if (g.d == 64)
       hipLaunchKernelGGL((attend_f32_kernel<64>), grid, block, 0, stream, a);
     else if (g.d == 128)
