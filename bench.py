@@ -14,8 +14,9 @@ resident in HBM before timing.
 
 Prints ONE JSON line.  `value` = attention TFLOP per chunk / wall time per
 chunk (everything in the step counted in the time).  `roofline` is the
-attention kernel alone (HIP events on the launch stream), against the bf16
-dense MFMA peak.  `cpu_baseline` times the fp64 oracle on a bounded sample.
+attention kernel alone (HIP events on the launch stream), against the dense
+MFMA peak of its arithmetic type (bf16, or fp8 for the fp8 workload).
+`cpu_baseline` times the fp64 oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -108,8 +109,8 @@ def main():
                     help="only run device-to-device copies of MIB MiB (scales PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: the chunk attention path has no multi-GPU sharding "
-              "in this build (heads would shard across GPUs; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU: the chunk attention path is single-GPU (its heads are "
+              "independent and would shard across GPUs without any exchange).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -7,7 +7,7 @@ generators in ``synth``.
 
 What it computes, and where the pages define it (pages cited by title and
 section; the pages carry no formula, so each step below is the plainest
-reading of the prose, listed with the other readings in the design notes):
+reading of the prose):
 
 * Bounded cache -- "Vidu S2 vs PixVerse R2" blog (orkas.ai), section "Choice 3:
   bounded memory" (选择三：有上限的记忆): the first blocks stay as permanent
