@@ -94,6 +94,8 @@ class Cache:
             raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous CUDA tensor")
+        if t.device != self.pool.device:
+            raise ValueError(f"{name} is on {t.device}, the cache on {self.pool.device}")
         return t.data_ptr()
 
     # ---- the C calls -----------------------------------------------------------
@@ -157,6 +159,8 @@ class Cache:
         if tile_idx is not None:
             if tile_idx.dtype != torch.int32 or not tile_idx.is_cuda or not tile_idx.is_contiguous():
                 raise ValueError("tile_idx must be a contiguous int32 CUDA tensor")
+            if self.pool is not None and tile_idx.device != self.pool.device:
+                raise ValueError(f"tile_idx is on {tile_idx.device}, the cache on {self.pool.device}")
             nt = -(-self.cfg.block_tokens // self.cfg.tile)
             if tuple(tile_idx.shape) != (self.cfg.n_heads, nt, k_row):
                 raise ValueError(f"tile_idx shape {tuple(tile_idx.shape)} != {(self.cfg.n_heads, nt, k_row)}")
