@@ -96,8 +96,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20, help="timed chunks")
     ap.add_argument("--warmup", type=int, default=3, help="untimed chunks")
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-heads", type=int, default=12,
-                    help="heads in the oracle sample, about 1 s of CPU time each at 540p (0 = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=24,
+                    help="heads in the oracle sample (24 = one whole 540p call, about 15 s on 16 "
+                         "host threads; 0 = skip)")
     ap.add_argument("--flat-chunks", type=int, default=0, metavar="N",
                     help="after the timed steps, time N more chunks one by one and report the latency slope")
     ap.add_argument("--fused-qkv", action="store_true",
@@ -404,7 +405,7 @@ def main():
         src_ms = [a.elapsed_time(b) for a, b in ev["source"]]
         res["source_append_ms_per_chunk"] = sum(src_ms) / len(src_ms)
     if args.cpu_heads > 0:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.n_heads))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
