@@ -54,6 +54,7 @@ struct AttnArgs {
   int n_slots;
   int aligned_last;   // 1: the last slot is frame-aligned (editing source frames)
   float scale_log2;   // log2(e) / sqrt(d)
+  float inv_hw;       // 1 / (lat_h * lat_w), rounded to fp32 on the host
   int n_qt;           // query tiles per head of this launch
   int n_full;         // workgroups that own a whole query tile
   int n_split;        // key-range pieces of each remaining tile (0: none)
@@ -228,8 +229,11 @@ void attend_bf16_kernel(AttnArgs a) {
   const int qh = qrem / a.lat_w, qw = qrem - qh * a.lat_w;
   const u16* qp = static_cast<const u16*>(a.q) + ((size_t)qrow * a.H + h) * D;
   // frame of key j = floor((j + 0.5) / hw) in fp32: exact, since j < 65536 keeps the rounding error
-  // below 0.01 / hw while (j + 0.5) / hw is at least 0.5 / hw from an integer
-  const float inv_hw = 1.0f / (float)a.hw;
+  // below 0.01 / hw while (j + 0.5) / hw is at least 0.5 / hw from an integer.  A kernel argument,
+  // so it stays in a scalar register: a value computed here would live in a vector register, be
+  // spilled, and be reloaded in the masking branch with a wait that also waits for the staging
+  // loads of the next block.
+  const float inv_hw = a.inv_hw;
 
   f32x16 acc[4];
 #pragma unroll
@@ -1122,6 +1126,7 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
     if (slots[l].aligned) return hipErrorInvalidValue;   // only the last slot may be frame-aligned
   if (a.aligned_last && (tile_idx || n_slots < 2)) return hipErrorInvalidValue;
   a.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)g.d));
+  a.inv_hw = 1.0f / (float)(g.lat_h * g.lat_w);
   a.rt = rt;
   a.part_o = plan.part_o;
   a.part_lse = plan.part_lse;
@@ -1186,6 +1191,7 @@ hipError_t launch_attend_fp8(const Geometry& g, const RopeTab& rt, const void* q
   a.n_slots = n_slots;
   a.aligned_last = 0;
   a.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)g.d));
+  a.inv_hw = 1.0f / (float)(g.lat_h * g.lat_w);
   a.rt = rt;
   a.part_o = plan.part_o;
   a.part_lse = plan.part_lse;
