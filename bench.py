@@ -184,13 +184,19 @@ def main():
     state = {"block": 0, "window": 0, "sinks": 0}
     history = []            # frames of the committed blocks the cache holds, logical order
 
+    host_us = {"evict": [], "promote": []}   # host time of the index-remap calls (no device work)
+
     def commit():
         b = state["block"]
         if state["sinks"] >= w.n_sink and w.n_window > 0 and state["window"] == w.n_window:
+            t0 = time.perf_counter()
             cache.evict()
+            host_us["evict"].append((time.perf_counter() - t0) * 1e6)
             state["window"] -= 1
             history.pop(state["sinks"])
+        t0 = time.perf_counter()
         cache.append("clean", None, None, b)
+        host_us["promote"].append((time.perf_counter() - t0) * 1e6)
         if state["sinks"] < w.n_sink:
             state["sinks"] += 1
             history.append(frames_of(b))
@@ -279,6 +285,18 @@ def main():
     dt = time.perf_counter() - t0
     if w.sparse_keep is not None:   # the last timed mask (later phases reuse the buffer)
         last_mask["idx"] = mask_buf["idx"].clone()
+
+    # host cost of the cache bookkeeping: evict and promote (index remaps, zero bytes moved) over
+    # the warm-up and timed chunks, and a relocation-policy call
+    def med(x):
+        x = sorted(x)
+        return x[len(x) // 2] if x else None
+    t0 = time.perf_counter()
+    for _ in range(100):
+        cache.relocate(w.policy)
+    cache_host = {"evict_median": med(host_us["evict"]), "promote_median": med(host_us["promote"]),
+                  "relocate_mean": (time.perf_counter() - t0) * 1e4, "calls": len(host_us["evict"]),
+                  "bytes_moved": 0}
 
     flat = None
     if args.flat_chunks > 0:
@@ -377,6 +395,7 @@ def main():
         "append_ms_per_call": avg_app,
         "append_gbps": append_bytes / (avg_app * 1e-3) / 1e9,
         "latency_flatness": flat,
+        "cache_host_us": cache_host,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": load_traffic(args.workload),
                      "kernel": ("attend_fp8_kernel<4>" if w.attn_fp8 else

@@ -805,22 +805,26 @@ void attend_fp8_kernel(AttnArgs a) {
   uint32_t qsc = 0x7f7f7f7fu;
   load_q8<0, 2>(rt, qp, qvalid, qf, qh, qw, hf, 0, q8, qsc);
 
-  // per-lane LDS byte offsets of the operand reads (two 16-byte chunks each)
+  // per-lane LDS byte offsets of the operand reads (two 16-byte chunks each).  The LDS serves a
+  // 16-byte read for 16 lanes at a time from 64 four-byte banks (256 bytes): rows of 128 bytes
+  // (K) put two rows in one bank line, so the chunk is swizzled with (row / 2) & 7; rows of 64
+  // bytes (V^T) put four, swizzled with (row / 4) & 3.  Each group of 16 lanes then reads 16
+  // different bank quads.
   int koff[2][2], voff[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) koff[c][u] = ln * 128 + 16 * ((4 * c + 2 * u + hf) ^ (ln & 7));
+    for (int u = 0; u < 2; ++u) koff[c][u] = ln * 128 + 16 * ((4 * c + 2 * u + hf) ^ ((ln >> 1) & 7));
 #pragma unroll
   for (int u = 0; u < 2; ++u) voff[u] = ln * 64 + 16 * ((2 * hf + u) ^ ((ln >> 2) & 3));
-  // staging: wave w moves K rows 8w..8w+7 and V^T rows 16w..16w+15 of the block
-  // staging: chunk C = NW * p + wave moves K rows 8C..8C+7 and V^T rows 16C..16C+15 of the block
+  // staging: chunk C = NW * p + wave moves K rows 8C..8C+7 and V^T rows 16C..16C+15 of the block,
+  // into the swizzled positions the reads above expect
   int stk[NSTG], stv[NSTG];
 #pragma unroll
   for (int p = 0; p < NSTG; ++p) {
     const int C = NW * p + wave;
     const int kr = 8 * C + (lane >> 3), vr = 16 * C + (lane >> 2);
-    stk[p] = kr * D + 16 * ((lane & 7) ^ (kr & 7));
+    stk[p] = kr * D + 16 * ((lane & 7) ^ ((kr >> 1) & 7));
     stv[p] = vr * KB + 16 * ((lane & 3) ^ ((vr >> 2) & 3));
   }
   const size_t kstride = (size_t)n_pad * D;   // bytes per head, K and V^T alike
