@@ -113,10 +113,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int VROWS = kTile / 2;        // V rows staged in LDS at a time (bf16 transpose)
   // one LDS buffer: first the pooled partial sums, then (bf16) half a tile of V rows; small
   // enough for 8 workgroups per CU, so a whole 540p launch is resident at once
-  constexpr int SMEM = SUB * D * 4 > VROWS * (D + 8) * 2 ? SUB * D * 4 : VROWS * (D + 8) * 2;
+  // V rows staged with a stride of D + 2 elements (an odd number of 4-byte words): the transpose
+  // reads rows 0, 4, 16, 20, ... of one column in a single instruction, and an odd stride sends
+  // them to distinct banks (a 16-byte-aligned stride cannot)
+  constexpr int VST = D + 2;
+  constexpr int SMEM = SUB * D * 4 > VROWS * VST * 2 ? SUB * D * 4 : VROWS * VST * 2;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   float (*red)[D] = reinterpret_cast<float (*)[D]>(smem);
-  u16 (*vl)[D + 8] = reinterpret_cast<u16 (*)[D + 8]>(smem);
+  u16 (*vl)[VST] = reinterpret_cast<u16 (*)[VST]>(smem);
 
   const int tid = threadIdx.x, j = blockIdx.x, h = blockIdx.y;
   const int grp = tid % GPR;
@@ -202,7 +206,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       for (int it = 0; it < NV; ++it) {
         const int row = (tid + 256 * it) / GPR;
         const bool ok = j * kTile + VROWS * hv + row < a.B;
-        *reinterpret_cast<uint4*>(&vl[row][grp * 8]) = ok ? v[it] : make_uint4(0, 0, 0, 0);
+        const uint4 x = ok ? v[it] : make_uint4(0, 0, 0, 0);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(&vl[row][grp * 8]);   // 4-byte aligned rows
+        dst[0] = x.x;
+        dst[1] = x.y;
+        dst[2] = x.z;
+        dst[3] = x.w;
       }
       __syncthreads();
 #pragma unroll
