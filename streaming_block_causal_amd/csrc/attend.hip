@@ -709,10 +709,12 @@ __device__ __forceinline__ void load_q8(const RopeTab rt, const u16* qp, bool va
   const int t = qf + delta;
 #pragma unroll
   for (int c = C0; c < C1; ++c) {
-    float x[32];
+    int eg[2];
+    // the two 32-channel groups one after the other (16 rotated values live at a time)
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int base = 64 * c + 32 * g + 16 * hf;
+      float x[16];
       if (valid) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -723,26 +725,24 @@ __device__ __forceinline__ void load_q8(const RopeTab rt, const u16* qp, bool va
             float cs, sn;
             rope_cs(rt, base / 2 + 4 * u + i, t, qh, qw, cs, sn);
             const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xffff0000u);
-            x[16 * g + 8 * u + 2 * i] = x0 * cs - x1 * sn;
-            x[16 * g + 8 * u + 2 * i + 1] = x0 * sn + x1 * cs;
+            x[8 * u + 2 * i] = x0 * cs - x1 * sn;
+            x[8 * u + 2 * i + 1] = x0 * sn + x1 * cs;
           }
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[16 * g + i] = 0.f;
+        for (int i = 0; i < 16; ++i) x[i] = 0.f;
       }
-    }
-    float am[2] = {0.f, 0.f};
+      float am = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) am[i >> 4] = fmaxf(am[i >> 4], fabsf(x[i]));
-    const int e0 = e8m0_of(swap_halves_max(am[0])), e1 = e8m0_of(swap_halves_max(am[1]));
-    const float sc0 = __uint_as_float((uint32_t)(127 - e0) << 23), sc1 = __uint_as_float((uint32_t)(127 - e1) << 23);
+      for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i]));
+      eg[g] = e8m0_of(swap_halves_max(am));
+      const float sc = __uint_as_float((uint32_t)(127 - eg[g]) << 23);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      q8[c][i] = (int)pack4_fp8(x[4 * i] * sc0, x[4 * i + 1] * sc0, x[4 * i + 2] * sc0, x[4 * i + 3] * sc0);
-      q8[c][4 + i] = (int)pack4_fp8(x[16 + 4 * i] * sc1, x[17 + 4 * i] * sc1, x[18 + 4 * i] * sc1,
-                                    x[19 + 4 * i] * sc1);
+      for (int i = 0; i < 4; ++i)
+        q8[c][4 * g + i] = (int)pack4_fp8(x[4 * i] * sc, x[4 * i + 1] * sc, x[4 * i + 2] * sc, x[4 * i + 3] * sc);
     }
+    const int e0 = eg[0], e1 = eg[1];
     const int e = hf ? e1 : e0;
     qsc = (qsc & ~(0xffu << (8 * c))) | ((uint32_t)(e + 127) << (8 * c));
   }
