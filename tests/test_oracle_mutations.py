@@ -142,3 +142,22 @@ def test_dropped_forced_tile_is_caught(monkeypatch):
     from tests.test_oracle_tilemask import test_c5_steady_state_sparsity
     with pytest.raises(AssertionError):
         test_c5_steady_state_sparsity()
+
+
+def test_ragged_tile_pooled_over_full_tile_is_caught(monkeypatch):
+    """Averaging a ragged last tile over 128 rows (zero pads counted) instead of its valid tokens."""
+    def padded_mean(x, tile=128):
+        return np.stack([x[a:b].sum(axis=0) / tile for a, b in tilemask.tile_bounds(x.shape[0], tile)])
+    monkeypatch.setattr(tilemask, "pooled", padded_mean)
+    from tests.test_oracle_tilemask import test_golden_kept_tiles_through_stream
+    with pytest.raises(AssertionError):
+        test_golden_kept_tiles_through_stream()
+
+
+def test_unrelocated_tile_scores_are_caught(monkeypatch):
+    """Scoring key tiles with block-local (un-relocated) vectors."""
+    orig = stream.relocated_head
+    monkeypatch.setattr(stream, "relocated_head", lambda w, stored, head, base: orig(w, stored, head, 0))
+    from tests.test_oracle_tilemask import test_golden_kept_tiles_through_stream
+    with pytest.raises(AssertionError):
+        test_golden_kept_tiles_through_stream()

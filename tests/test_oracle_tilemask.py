@@ -5,6 +5,7 @@ from" (block-sparse attention above 90% sparsity).  Mask recipe: top-k of
 mean-pooled tile scores with forced tiles (stated reading in oracle/tilemask.py).
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -71,8 +72,13 @@ def test_keep_all_equals_dense():
         np.testing.assert_allclose(l, ld, atol=1e-12)
 
 
-def test_gather_equals_mask_and_forced_present():
-    w = SMALL.replace(sparse_keep=0.25)
+# B = 480: three full tiles and a ragged one of 96 tokens
+RAGGED = synth.tiny(5, n_heads=2, lat_h=8, lat_w=20, n_chunks=6, n_steps=1)
+
+
+@pytest.mark.parametrize("base", [SMALL, RAGGED], ids=["full_tiles", "ragged_tile"])
+def test_gather_equals_mask_and_forced_present(base):
+    w = base.replace(sparse_keep=0.25)
     st = stream.Stream(w)
     for n in (0, 1, 4, 5):
         o, lse, kept = st.call(n, 1)
@@ -104,3 +110,64 @@ def test_c5_steady_state_sparsity():
     frac = sum(len(r) for r in rows) / (48 * 240)
     assert frac < 0.10
     assert all(0 in r and (4 * 48 + i) in r for i, r in enumerate(rows))
+
+
+# ---- hand-derived worked example: a ragged key tile, a query tile that is ragged too, and a sink
+# slot whose relocation turns the time pair by one radian (tests/golden/tilemask_ragged_relocated.txt)
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tilemask_ragged_relocated.txt")
+
+
+def _golden():
+    rec = {}
+    with open(GOLDEN) as fh:
+        for ln in fh:
+            if ln.startswith("#") or not ln.strip():
+                continue
+            key, vals = ln.split(":", 1)
+            rec[key.strip()] = [float(x) for x in vals.split()]
+    return rec
+
+
+def _golden_case():
+    g = _golden()
+    d = int(g["d"][0])
+    frames, lat_h, lat_w = (int(x) for x in g["grid"])
+    w = synth.tiny(5, name="tilemask_golden", n_heads=1, head_dim=d, frames=frames, lat_h=lat_h,
+                   lat_w=lat_w, n_sink=1, n_window=0, n_chunks=2, n_steps=1, dtype="f32", scale=1.0,
+                   sparse_keep=g["keep"][0], policy="s1")
+    B = w.block_tokens
+
+    def fill(name):
+        x = np.zeros((B, 1, d), dtype=np.float32)
+        for j, (a, b) in enumerate(tilemask.tile_bounds(B)):
+            pat = np.asarray(g[f"pattern {name} {j}"], dtype=np.float32).reshape(-1, 2)
+            x[a:b, 0, 0:2] = pat[np.arange(b - a) % len(pat)]
+        return x
+    zero = np.zeros((B, 1, d), dtype=np.float32)
+    return g, w, fill("q"), fill("k_sink"), fill("k_cur"), zero
+
+
+def test_golden_tile_scores_ragged_and_relocated():
+    """Pooled scores and kept tiles of the hand-worked example, from the oracle's relocation and
+    tilemask.build."""
+    g, w, q, k_sink, k_cur, _ = _golden_case()
+    bases = stream.Stream(w).bases(1)
+    assert bases == [0, 1]
+    q_rel = stream.relocated_head(w, q, 0, bases[1])
+    k_rel = [stream.relocated_head(w, k_sink, 0, bases[0]), stream.relocated_head(w, k_cur, 0, bases[1])]
+    kept, scores, budget = tilemask.build(q_rel, k_rel, ["sink", "current"], g["keep"][0], w.tile)
+    want = np.array([g["scores_x_sqrt_d 0"], g["scores_x_sqrt_d 1"]]) / math.sqrt(w.head_dim)
+    np.testing.assert_allclose(scores, want, rtol=0, atol=1e-12)
+    assert budget == 3
+    assert kept == [[int(x) for x in g["kept 0"]], [int(x) for x in g["kept 1"]]]
+
+
+def test_golden_kept_tiles_through_stream():
+    """The same example through the stream oracle: its mask (and the attention restricted to it)."""
+    g, w, q, k_sink, k_cur, v0 = _golden_case()
+    st = stream.Stream(w, contents=lambda b, kind: (k_sink, v0) if b == 0 else None)
+    o, lse, kept = st.call(1, 1, current=(q, k_cur, v0))
+    assert kept[0] == [[int(x) for x in g["kept 0"]], [int(x) for x in g["kept 1"]]]
+    assert np.all(o == 0.0)                          # V is zero
+    # every query sees 128 + 32 + (its diagonal tile) keys -> LSE = log(sum exp(score)) is finite
+    assert np.all(np.isfinite(lse))
