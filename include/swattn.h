@@ -112,6 +112,11 @@ typedef struct {
   int32_t sparse;           /* 0 | 1: keep pooled key-tile means for sw_build_tile_mask (bf16 only) */
   sw_dtype dtype;           /* storage and input dtype */
   double rope_theta;        /* RoPE base, > 1 (10000 is the usual value) */
+  int32_t rope_pairs_t;     /* rotation pairs of the time, height and width axes; all three 0 =  */
+  int32_t rope_pairs_h;     /* the default split (see the RoPE layout below); otherwise each >= 0 */
+  int32_t rope_pairs_w;     /* and t + h + w = head_dim / 2 (SW_ERR_INVALID_ARG), t <= 24 for bf16
+                               and fp8 caches (SW_ERR_UNSUPPORTED: their attention re-rotates only
+                               the first 48 dims of a query when it enters a slot) */
   sw_rope_policy policy;    /* initial relocation policy */
   int32_t tile;             /* block-sparse tile edge; must be 128 */
   int32_t editing;          /* 0 | 1: frame-aligned editing (a source staging buffer; dense only;
@@ -120,9 +125,10 @@ typedef struct {
 
 /* RoPE layout (pages name 3D RoPE over (t, h, w) without details -- Vidu S2
  * paper read, abbreviation table): P = d/2 pairs, pair p rotates dims
- * (2p, 2p+1); time gets P - 2*floor(P/3) pairs, then height and width
- * floor(P/3) each; inside an axis with P_a pairs, pair j turns by
- * pos * theta^(-j/P_a). */
+ * (2p, 2p+1); the first P_t pairs turn with time, the next P_h with the row,
+ * the last P_w with the column.  Default split (rope_pairs_* all 0): P_h = P_w
+ * = floor(P/3), P_t = P - 2*floor(P/3).  Inside an axis with P_a pairs, pair j
+ * turns by pos * theta^(-j/P_a). */
 
 typedef struct {
   int32_t role;          /* 0 sink, 1 window, 2 current, 3 source (editing) */
@@ -206,11 +212,15 @@ sw_status sw_tile_mask_budget(const sw_cache* c, float keep_frac, int32_t* k_row
  * 128-query tile, score every key tile by the dot product of
  * mean relocated rotated query and key vectors / sqrt(d), keep key tile 0 of
  * the first sink (if any) and the diagonal current tile, fill up to the budget
- * with the highest scores (ties -> lower index).  Writes ascending linear key
- * tile indices (slot * ceil(B/128) + tile) to tile_idx_out
- * [H][ceil(B/128)][k_cap] (device int32); *k_row_out (host) = budget.
- * Needs a sparse bf16 cache with a staged current block. */
-sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, float keep_frac,
+ * with the highest scores (ties -> lower index).  The keys scored are the ones
+ * the attention of the same step reads: with TwinCache the noisy copies for
+ * SW_STEP_INTERMEDIATE, the clean ones for SW_STEP_FINAL (blog, "Choice 3").
+ * Writes ascending linear key tile indices (slot * ceil(B/128) + tile) to
+ * tile_idx_out [H][ceil(B/128)][k_cap] (device int32); when k_cap exceeds the
+ * budget the rest of each row is -1; *k_row_out (host) = budget.  Needs a
+ * sparse bf16 cache with a staged current block; SW_ERR_CAPACITY if k_cap <
+ * budget. */
+sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, sw_step_kind step, float keep_frac,
                              int32_t* tile_idx_out, int32_t k_cap, int32_t* k_row_out);
 
 /* One denoising step's chunk attention for the staged current block:
@@ -225,10 +235,11 @@ sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, float keep_frac,
  * in the cache dtype; lse_out (nullable) [H][B] fp32 natural-log sum of
  * exp(score) per query.  tile_idx == NULL: dense; otherwise block-sparse over
  * the key tiles listed in tile_idx [H][ceil(B/128)][k_row] (as written by
- * sw_build_tile_mask; may be unsorted but are then visited in the given
- * order; entries outside [0, n_key_tiles), such as the -1 padding a mask
- * built with k_cap > budget carries, are skipped: pass k_row = k_cap for such
- * a list).  step selects the TwinCache copy. */
+ * sw_build_tile_mask).  A row is read in order and each key tile counts at
+ * most once: an entry outside [0, n_key_tiles) (such as the -1 padding of a
+ * mask built with k_cap > budget: pass k_row = k_cap for such a list) or not
+ * above the last entry taken from its row (a repeat, or an entry out of
+ * ascending order) is skipped.  step selects the TwinCache copy. */
 sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step,
                           const int32_t* tile_idx, int32_t k_row, void* out, float* lse_out);
 
@@ -277,6 +288,20 @@ sw_status sw_graph_destroy(sw_graph* g);
 
 /* Chunks after which the ring layout repeats in steady state (n_window + 1). */
 sw_status sw_cache_ring_period(const sw_cache* c, int32_t* period);
+
+/* ---- measurement aid (not a step of the method) ------------------------------
+ * The sustained matrix-core rate of the device, for reporting attention throughput
+ * against a measured peak beside the datasheet one.  Enqueues on hip_stream one launch
+ * of 8 waves per compute unit, each running four independent chains of `iters` MFMAs
+ * with operands in registers: v_mfma_f32_32x32x16_bf16 (dtype SW_BF16) or
+ * v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 operands (SW_FP8).  sink: device buffer of
+ * sink_floats >= 8 * (compute units) floats the waves write one value each into
+ * (keeps the chains live).  *flops_out (host) = the launch's flops, for the caller to
+ * divide by its measured duration.  SW_ERR_INVALID_ARG for NULL pointers, iters < 1 or
+ * another dtype; SW_ERR_CAPACITY for a short sink; SW_ERR_HIP if the launch fails.
+ * Sets no error message. */
+sw_status sw_probe_mfma(void* hip_stream, sw_dtype dtype, int32_t iters, float* sink, int32_t sink_floats,
+                        double* flops_out);
 
 #ifdef __cplusplus
 }

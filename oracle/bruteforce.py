@@ -48,10 +48,13 @@ def instant(w: synth.Workload, b: int, f):
     return sum(synth.frames_of(w, c) for c in range(b)) + f
 
 
-def _pair_angles(t, h, wcol, head_dim, theta):
+def _pair_angles(t, h, wcol, head_dim, theta, split=None):
     p_all = head_dim // 2
-    ph = pw = p_all // 3
-    pt = p_all - ph - pw
+    if split is None:
+        ph = pw = p_all // 3
+        pt = p_all - ph - pw
+    else:
+        pt, ph, pw = split
     out = np.empty(t.shape + (p_all,), dtype=np.float64)
     for p in range(p_all):
         if p < pt:
@@ -63,9 +66,9 @@ def _pair_angles(t, h, wcol, head_dim, theta):
     return out
 
 
-def _rope_complex(x, t, h, wcol, theta):
+def _rope_complex(x, t, h, wcol, theta, split=None):
     z = x[..., 0::2] + 1j * x[..., 1::2]
-    z = z * np.exp(1j * _pair_angles(t, h, wcol, x.shape[-1], theta))
+    z = z * np.exp(1j * _pair_angles(t, h, wcol, x.shape[-1], theta, split))
     y = np.empty_like(x)
     y[..., 0::2], y[..., 1::2] = z.real, z.imag
     return y
@@ -97,12 +100,12 @@ def chunk(w: synth.Workload, n: int, s: int, seed: int = 0, contents=None):
         t0 = times.get(b, 0)
         f, hh, wc = grid(b)
         ks.append(_rope_complex(synth.as_f64(w, k_st), (t0 + f)[:, None], hh[:, None], wc[:, None],
-                                w.rope_theta))
+                                w.rope_theta, w.rope_split))
         vs.append(synth.as_f64(w, v_st))
         key_block.append(np.full(f.size, b))
     f, hh, wc = grid(n)
     q = _rope_complex(synth.as_f64(w, q_st), (times[n] + f)[:, None], hh[:, None], wc[:, None],
-                      w.rope_theta)
+                      w.rope_theta, w.rope_split)
     k = np.concatenate(ks, 0)
     v = np.concatenate(vs, 0)
     kb = np.concatenate(key_block)
@@ -116,7 +119,7 @@ def chunk(w: synth.Workload, n: int, s: int, seed: int = 0, contents=None):
             t0 = times.get(b, 0)
             fb, hb, wb = grid(b)
             sk.append(_rope_complex(synth.as_f64(w, k_src), (t0 + fb)[:, None], hb[:, None], wb[:, None],
-                                    w.rope_theta))
+                                    w.rope_theta, w.rope_split))
             sv.append(synth.as_f64(w, v_src))
             s_inst.append(instant(w, b, fb))
         s_inst = np.concatenate(s_inst)

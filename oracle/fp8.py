@@ -83,7 +83,7 @@ def key_local(w, stored_k: np.ndarray, head: int, as_f64) -> np.ndarray:
     """Dequantised K [B, d] of one head: rotated at block-local positions, then quantised."""
     x = as_f64(w, stored_k[:, head, :])
     f, hh, ww = rope.block_grid(stored_k.shape[0] // (w.lat_h * w.lat_w), w.lat_h, w.lat_w)
-    return quantize_groups(rope.rotate(x, rope.angles(f, hh, ww, w.head_dim, w.rope_theta)))
+    return quantize_groups(rope.rotate(x, rope.angles(f, hh, ww, w.head_dim, w.rope_theta, w.rope_split)))
 
 
 def query_for_slot(w, stored_q: np.ndarray, head: int, delta: int, as_f64) -> np.ndarray:
@@ -91,7 +91,7 @@ def query_for_slot(w, stored_q: np.ndarray, head: int, delta: int, as_f64) -> np
     relocation: time base of the current block minus that of the slot), then quantised."""
     x = as_f64(w, stored_q[:, head, :])
     f, hh, ww = rope.block_grid(stored_q.shape[0] // (w.lat_h * w.lat_w), w.lat_h, w.lat_w)
-    return quantize_groups(rope.rotate(x, rope.angles(f + delta, hh, ww, w.head_dim, w.rope_theta)))
+    return quantize_groups(rope.rotate(x, rope.angles(f + delta, hh, ww, w.head_dim, w.rope_theta, w.rope_split)))
 
 
 def attend_head(w, head: int, q_stored, slots, bases, rows, as_f64, row_block: int = 512):

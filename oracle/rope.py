@@ -9,8 +9,9 @@ range seen in training, however long the session runs.
 The pages fix neither the split of the head dimension over (t, h, w), nor the
 frequencies, nor the relocation formula.  Readings used (plainest ones):
 
-* P = d/2 rotation pairs; pair p rotates dims (2p, 2p+1).  Height and width
-  get floor(P/3) pairs each, time gets the rest, in the order t, h, w.
+* P = d/2 rotation pairs; pair p rotates dims (2p, 2p+1), time pairs first,
+  then height, then width.  By default height and width get floor(P/3) pairs
+  each and time the rest; a workload may give its own split (P_t, P_h, P_w).
 * Inside an axis with P_a pairs, pair j turns at omega_j = theta^(-j/P_a),
   theta = 10000, by angle pos * omega_j; (x0, x1) -> (x0 cos - x1 sin,
   x0 sin + x1 cos).
@@ -24,11 +25,16 @@ from __future__ import annotations
 import numpy as np
 
 
-def axis_split(head_dim: int):
-    """(pairs for time, height, width)."""
+def axis_split(head_dim: int, split=None):
+    """(pairs for time, height, width): the given split, or the default one."""
     if head_dim % 2:
         raise ValueError("head_dim must be even")
     p = head_dim // 2
+    if split is not None:
+        pt, ph, pw = (int(x) for x in split)
+        if min(pt, ph, pw) < 0 or pt + ph + pw != p:
+            raise ValueError(f"RoPE split {split} does not cover {p} pairs")
+        return pt, ph, pw
     third = p // 3
     return p - 2 * third, third, third
 
@@ -38,9 +44,9 @@ def axis_frequencies(n_pairs: int, theta: float) -> np.ndarray:
     return np.power(float(theta), -j / n_pairs) if n_pairs else np.zeros(0)
 
 
-def angles(t, h, w, head_dim: int, theta: float = 10000.0) -> np.ndarray:
+def angles(t, h, w, head_dim: int, theta: float = 10000.0, split=None) -> np.ndarray:
     """Rotation angle of every pair for tokens at positions (t, h, w) -> [..., d/2]."""
-    pt, ph, pw = axis_split(head_dim)
+    pt, ph, pw = axis_split(head_dim, split)
     t = np.asarray(t, dtype=np.float64)[..., None]
     h = np.asarray(h, dtype=np.float64)[..., None]
     w = np.asarray(w, dtype=np.float64)[..., None]
@@ -98,8 +104,8 @@ def relocation_bases_frames(policy: str, sink_frames, window_frames, current_fra
 
 
 def rotate_block(x: np.ndarray, base: int, frames: int, lat_h: int, lat_w: int,
-                 theta: float = 10000.0) -> np.ndarray:
+                 theta: float = 10000.0, split=None) -> np.ndarray:
     """RoPE of a whole block [B, H, d] whose first frame sits at time `base`."""
     f, h, w = block_grid(frames, lat_h, lat_w)
-    ang = angles(base + f, h, w, x.shape[-1], theta)      # [B, d/2]
+    ang = angles(base + f, h, w, x.shape[-1], theta, split)      # [B, d/2]
     return rotate(x, ang[:, None, :])

@@ -142,7 +142,7 @@ def relocated_head(w: synth.Workload, stored: np.ndarray, head: int, base: int) 
     """[B, d] float64 RoPE of one head of a stored block placed at time `base`."""
     x = synth.as_f64(w, stored[:, head, :])
     f, hh, ww = rope.block_grid(stored.shape[0] // (w.lat_h * w.lat_w), w.lat_h, w.lat_w)
-    return rope.rotate(x, rope.angles(base + f, hh, ww, w.head_dim, w.rope_theta))
+    return rope.rotate(x, rope.angles(base + f, hh, ww, w.head_dim, w.rope_theta, w.rope_split))
 
 
 def _one_head(job, h):

@@ -6,7 +6,7 @@ in libswattn's HIP kernels.
 from __future__ import annotations
 
 import dataclasses
-from typing import Optional
+from typing import Optional, Tuple
 
 import torch
 
@@ -37,6 +37,7 @@ class CacheConfig:
     policy: str = "s1"
     tile: int = 128
     editing: bool = False
+    rope_pairs: Optional[Tuple[int, int, int]] = None   # (time, height, width) pairs; None: default split
 
     @property
     def block_tokens(self) -> int:
@@ -47,7 +48,8 @@ class CacheConfig:
             n_heads=self.n_heads, head_dim=self.head_dim, frames_per_block=self.frames_per_block,
             lat_h=self.lat_h, lat_w=self.lat_w, n_sink=self.n_sink, n_window=self.n_window,
             twin=int(self.twin), sparse=int(self.sparse), dtype=_DTYPES[self.dtype][0],
-            rope_theta=self.rope_theta, policy=_POLICY[self.policy], tile=self.tile, editing=int(self.editing))
+            rope_theta=self.rope_theta, policy=_POLICY[self.policy], tile=self.tile, editing=int(self.editing),
+            **dict(zip(("rope_pairs_t", "rope_pairs_h", "rope_pairs_w"), self.rope_pairs or (0, 0, 0))))
 
 
 class Cache:
@@ -67,9 +69,13 @@ class Cache:
             self.handle = native.sw_cache_create(self._c, 0, 0, 0)
         else:
             self.stream = stream if stream is not None else torch.cuda.current_stream(device)
-            self.pool = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+            # the pool belongs to the stream its kernels run on: the allocator hands it back only
+            # after that stream's work
+            with torch.cuda.stream(self.stream):
+                self.pool = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
             self.handle = native.sw_cache_create(self._c, self.pool.data_ptr(), self.nbytes,
                                                  self.stream.cuda_stream)
+        self._capturing = False
 
     def close(self):
         if getattr(self, "handle", None):
@@ -98,6 +104,29 @@ class Cache:
             raise ValueError(f"{name} is on {t.device}, the cache on {self.pool.device}")
         return t.data_ptr()
 
+    # ---- stream order ------------------------------------------------------------
+    # The kernels run on the cache's stream.  When the caller's current stream is another one,
+    # the cache's stream first waits for the current stream (inputs written there), and after the
+    # call the current stream waits for the cache's (outputs read there); tensors the kernels use
+    # are recorded on the cache's stream so that the allocator does not reuse them early.  Not
+    # while a graph is being recorded: the recording covers the cache's stream only.
+    def _enter(self):
+        if self.device is None or self._capturing:
+            return None
+        cur = torch.cuda.current_stream(self.pool.device)
+        if cur == self.stream:
+            return None
+        self.stream.wait_stream(cur)
+        return cur
+
+    def _leave(self, cur, *tensors):
+        if cur is None:
+            return
+        for t in tensors:
+            if isinstance(t, torch.Tensor):
+                t.record_stream(self.stream)
+        cur.wait_stream(self.stream)
+
     # ---- the C calls -----------------------------------------------------------
     def shape_of(self, frames: int):
         return (frames * self.cfg.lat_h * self.cfg.lat_w, self.cfg.n_heads, self.cfg.head_dim)
@@ -108,10 +137,12 @@ class Cache:
         shape = self.shape_of(n_frames) if n_frames is not None else self.shape
         kp = self._tensor(k, "k", shape=shape) if k is not None else 0
         vp = self._tensor(v, "v", shape=shape) if v is not None else 0
+        cur = self._enter()
         if n_frames is None:
             native.sw_cache_append_block(self.handle, KIND[kind], kp, vp, block_id)
         else:
             native.sw_cache_append_block_frames(self.handle, KIND[kind], kp, vp, block_id, n_frames)
+        self._leave(cur, k, v)
         if kind == "current":
             self.cur_frames = self.cfg.frames_per_block if n_frames is None else n_frames
 
@@ -124,10 +155,12 @@ class Cache:
         if q_out is None and self.device is not None:
             q_out = torch.empty(shape, dtype=self.torch_dtype, device=self.device)
         qkv_shape = (shape[0], 3, shape[1], shape[2])
-        native.sw_cache_append_qkv(self.handle, self._tensor(qkv, "qkv", shape=qkv_shape),
-                                   self._tensor(gamma_q, "gamma_q", torch.float32, (shape[2],)),
-                                   self._tensor(gamma_k, "gamma_k", torch.float32, (shape[2],)), eps,
-                                   self._tensor(q_out, "q_out", shape=shape), block_id, n_frames)
+        args = (self._tensor(qkv, "qkv", shape=qkv_shape), self._tensor(gamma_q, "gamma_q", torch.float32, (shape[2],)),
+                self._tensor(gamma_k, "gamma_k", torch.float32, (shape[2],)), eps,
+                self._tensor(q_out, "q_out", shape=shape), block_id, n_frames)
+        cur = self._enter()
+        native.sw_cache_append_qkv(self.handle, *args)
+        self._leave(cur, qkv, gamma_q, gamma_k, q_out)
         self.cur_frames = n_frames
         return q_out
 
@@ -141,13 +174,17 @@ class Cache:
         return native.sw_tile_mask_budget(self.handle, keep_frac)
 
     def build_tile_mask(self, q: torch.Tensor, keep_frac: float, out: Optional[torch.Tensor] = None,
-                        k_cap: Optional[int] = None):
+                        k_cap: Optional[int] = None, step: str = "final"):
+        """Tile mask of this step's queries over the keys `step` reads (see sw_build_tile_mask)."""
         nt = -(-self.cfg.block_tokens // self.cfg.tile)
         k_cap = k_cap or self.mask_budget(keep_frac)
         if out is None:
             out = torch.empty((self.cfg.n_heads, nt, k_cap), dtype=torch.int32, device=self.device)
         op = self._tensor(out, "tile_idx_out", torch.int32, (self.cfg.n_heads, nt, k_cap))
-        k_row = native.sw_build_tile_mask(self.handle, self._tensor(q, "q"), keep_frac, op, k_cap)
+        qp = self._tensor(q, "q")
+        cur = self._enter()
+        k_row = native.sw_build_tile_mask(self.handle, qp, STEP[step], keep_frac, op, k_cap)
+        self._leave(cur, q, out)
         return out, k_row
 
     def attend(self, q: torch.Tensor, step: str = "final", tile_idx: Optional[torch.Tensor] = None,
@@ -166,8 +203,10 @@ class Cache:
                 raise ValueError(f"tile_idx shape {tuple(tile_idx.shape)} != {(self.cfg.n_heads, nt, k_row)}")
             tp = tile_idx.data_ptr()
         lp = self._tensor(lse, "lse", torch.float32, (self.cfg.n_heads, shape[0])) if lse is not None else 0
-        native.sw_chunk_attend(self.handle, self._tensor(q, "q", shape=shape), STEP[step], tp, k_row,
-                               self._tensor(out, "out", shape=shape), lp)
+        qp, outp = self._tensor(q, "q", shape=shape), self._tensor(out, "out", shape=shape)
+        cur = self._enter()
+        native.sw_chunk_attend(self.handle, qp, STEP[step], tp, k_row, outp, lp)
+        self._leave(cur, q, out, lse, tile_idx)
         return out
 
     def inspect(self):
@@ -182,7 +221,9 @@ class Cache:
         out_dtype = torch.float32 if self.cfg.dtype == "fp8" else self.torch_dtype   # fp8: dequantised
         k = torch.empty(self.shape_of(frames), dtype=out_dtype, device=self.device)
         v = torch.empty_like(k)
+        cur = self._enter()
         native.sw_cache_read_slot(self.handle, logical_slot, KIND[kind], k.data_ptr(), v.data_ptr())
+        self._leave(cur, k, v)
         return k, v
 
     # ---- graph replay (see sw_graph_begin) ------------------------------------------
@@ -192,8 +233,10 @@ class Cache:
     def graph_begin(self):
         """Start recording this cache's stream; pass `out=` to attend while recording (no allocation)."""
         native.sw_graph_begin(self.handle)
+        self._capturing = True
 
     def graph_end(self) -> "Graph":
+        self._capturing = False
         return Graph(native.sw_graph_end(self.handle))
 
 

@@ -117,16 +117,18 @@ __device__ __forceinline__ void load_q(const RopeTab rt, const u16* qp, bool val
 }
 
 // Sparse schedule: position i -> (slot, 64-key block, keys in the block) from the two halves of
-// each listed 128-key tile (every slot holds B keys).  Returns false for entries to skip (half of
-// a short last tile, or an invalid tile index).
-__device__ __forceinline__ bool block_at(const int32_t* list, int B, int n_slots, int nt, int nkb, int i, int& sl,
-                                         int& kb, int& kvalid) {
+// each listed 128-key tile (every slot holds B keys).  Returns false for entries to skip: half of
+// a short last tile, a tile index outside the cache, or one not above the last tile taken from the
+// row (`last`, updated after a tile's second half) -- so a repeated tile never counts twice.
+__device__ __forceinline__ bool block_at(const int32_t* list, int B, int n_slots, int nt, int nkb, int i, int& last,
+                                         int& sl, int& kb, int& kvalid) {
   // the list is read-only during the launch and its address is uniform: a scalar (constant
   // address space) load, counted on lgkmcnt.  A vector load here would be waited for with
   // vmcnt(0), which also waits for the staging loads of the next block issued just before.
   const int tix = *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
       reinterpret_cast<uintptr_t>(list + (i >> 1)));
-  if (tix < 0 || tix >= n_slots * nt) return false;   // never read outside the cache
+  if (tix < 0 || tix >= n_slots * nt || tix <= last) return false;   // never read outside the cache
+  if (i & 1) last = tix;
   sl = tix / nt;
   kb = 2 * (tix - sl * nt) + (i & 1);
   kvalid = B - kb * KB;
@@ -416,9 +418,10 @@ void attend_bf16_kernel(AttnArgs a) {
     ckb += rem;
   }
   // the schedule entry at or after position q (q is left on it): slot, block, keys in the block
+  int last_tile = -1;   // sparse: the last tile taken from the row
   auto lookup = [&](int& q, int& sl, int& kb, int& kv) {
     if (SPARSE) {
-      while (q < i1 && !block_at(list, B, n_slots, nt, nkb, q, sl, kb, kv)) ++q;
+      while (q < i1 && !block_at(list, B, n_slots, nt, nkb, q, last_tile, sl, kb, kv)) ++q;
     } else if (q < i1) {
       while (ckb >= cnb && csl + 1 < n_slots) enter(csl + 1);   // (skips empty slots)
       sl = csl;
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// fp32 kernel: one thread per query, keys broadcast from LDS, 16-key sub-blocks
+// fp32 kernel: four lanes per query (a quarter of the dimensions each), keys broadcast from LDS
 // ------------------------------------------------------------------------------------
 template <int DD>
 __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs a) {

@@ -112,9 +112,21 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
   if (c.editing && (long long)c.n_sink + c.n_window + 2 > kMaxSlots)
     return fail(SW_ERR_SHAPE, "n_sink + n_window + 2 = %d exceeds %d with editing", c.n_sink + c.n_window + 2,
                 kMaxSlots);
-  // the bf16 attention kernel re-rotates only the first 24 pairs per slot: time pairs must fit
-  if (c.dtype != SW_F32 && (c.head_dim / 2) - 2 * ((c.head_dim / 2) / 3) > 24)
-    return fail(SW_ERR_UNSUPPORTED, "time RoPE pairs exceed 24");
+  // RoPE split over (t, h, w): all zero = the default (time gets the remainder of thirds)
+  const int pairs = c.head_dim / 2;
+  int pt = pairs - 2 * (pairs / 3), ph = pairs / 3, pw = pairs / 3;
+  if (c.rope_pairs_t != 0 || c.rope_pairs_h != 0 || c.rope_pairs_w != 0) {
+    if (c.rope_pairs_t < 0 || c.rope_pairs_h < 0 || c.rope_pairs_w < 0 ||
+        (long long)c.rope_pairs_t + c.rope_pairs_h + c.rope_pairs_w != pairs)
+      return fail(SW_ERR_INVALID_ARG, "rope_pairs_t/h/w = %d/%d/%d must be >= 0 and sum to head_dim / 2 = %d",
+                  c.rope_pairs_t, c.rope_pairs_h, c.rope_pairs_w, pairs);
+    pt = c.rope_pairs_t;
+    ph = c.rope_pairs_h;
+    pw = c.rope_pairs_w;
+  }
+  // the bf16 and fp8 attention kernels re-rotate only the first 24 pairs of a query per slot
+  if (c.dtype != SW_F32 && pt > 24)
+    return fail(SW_ERR_UNSUPPORTED, "%d time RoPE pairs exceed the 24 the bf16 / fp8 kernels re-rotate", pt);
   const long long B = (long long)c.frames_per_block * c.lat_h * c.lat_w;
   if (B > 65536) return fail(SW_ERR_SHAPE, "block of %lld tokens exceeds 65536", B);
   Geometry& g = L->g;
@@ -134,9 +146,9 @@ sw_status make_layout(const sw_cache_config* cfg, Layout* L) {
   L->pooled_bytes = c.sparse ? align256((size_t)g.H * g.nt * g.d * sizeof(float)) : 0;
   L->P = c.n_sink + c.n_window + 1;
   L->t_len = L->P * g.F;
-  const int pairs = g.d / 2;
-  L->ph = L->pw = pairs / 3;
-  L->pt = pairs - 2 * (pairs / 3);
+  L->pt = pt;
+  L->ph = ph;
+  L->pw = pw;
   L->table_floats = 2 * ((size_t)L->t_len * L->pt + (size_t)g.lat_h * L->ph + (size_t)g.lat_w * L->pw);
   const int copies = c.twin ? 2 : 1;
   L->ws_bytes = c.dtype != SW_F32
@@ -635,9 +647,11 @@ sw_status sw_tile_mask_budget(const sw_cache* c, float keep_frac, int32_t* k_row
   return SW_OK;
 }
 
-sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, float keep_frac, int32_t* tile_idx_out,
-                             int32_t k_cap, int32_t* k_row_out) {
+sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, sw_step_kind step, float keep_frac,
+                             int32_t* tile_idx_out, int32_t k_cap, int32_t* k_row_out) {
   if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  if (step != SW_STEP_INTERMEDIATE && step != SW_STEP_FINAL)
+    return fail(SW_ERR_INVALID_ARG, "unknown step kind %d", (int)step);
   sw_status st = check_ptr(q_raw, "q_raw");
   if (st == SW_OK) st = check_ptr(tile_idx_out, "tile_idx_out");
   if (st == SW_OK) st = check_ptr(k_row_out, "k_row_out");
@@ -654,10 +668,13 @@ sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, float keep_frac, in
   const std::vector<Entry> hist = history(c);
   const std::vector<int> b = bases_of(c);
   const int n_slots = (int)hist.size() + 1;
+  // score the keys this step's attention reads: the noisy history copies on intermediate TwinCache
+  // steps, the clean ones otherwise; the current block has one copy
+  const bool noisy = c->cfg.twin && step == SW_STEP_INTERMEDIATE;
   const float* pooled[kMaxSlots];
   int deltas[kMaxSlots];
   for (int l = 0; l < n_slots; ++l) {
-    pooled[l] = l + 1 < n_slots ? c->pc[hist[l].phys] : c->pc[c->staging];
+    pooled[l] = l + 1 < n_slots ? (noisy ? c->pn[hist[l].phys] : c->pc[hist[l].phys]) : c->pc[c->staging];
     deltas[l] = b.back() - b[l];
   }
   const hipError_t e = launch_tile_mask(c->L.g, c->rt, q_raw, pooled, deltas, n_slots, !c->sinks.empty(),

@@ -31,7 +31,9 @@ class sw_cache_config(ctypes.Structure):
         ("frames_per_block", ctypes.c_int32), ("lat_h", ctypes.c_int32), ("lat_w", ctypes.c_int32),
         ("n_sink", ctypes.c_int32), ("n_window", ctypes.c_int32),
         ("twin", ctypes.c_int32), ("sparse", ctypes.c_int32),
-        ("dtype", ctypes.c_int), ("rope_theta", ctypes.c_double), ("policy", ctypes.c_int),
+        ("dtype", ctypes.c_int), ("rope_theta", ctypes.c_double),
+        ("rope_pairs_t", ctypes.c_int32), ("rope_pairs_h", ctypes.c_int32), ("rope_pairs_w", ctypes.c_int32),
+        ("policy", ctypes.c_int),
         ("tile", ctypes.c_int32), ("editing", ctypes.c_int32),
     ]
 
@@ -71,7 +73,7 @@ def lib() -> ctypes.CDLL:
             "sw_cache_evict": ([H], ctypes.c_int),
             "sw_rope_relocate": ([H, ctypes.c_int], ctypes.c_int),
             "sw_tile_mask_budget": ([H, F32, ctypes.POINTER(I32)], ctypes.c_int),
-            "sw_build_tile_mask": ([H, P, F32, P, I32, ctypes.POINTER(I32)], ctypes.c_int),
+            "sw_build_tile_mask": ([H, P, ctypes.c_int, F32, P, I32, ctypes.POINTER(I32)], ctypes.c_int),
             "sw_chunk_attend": ([H, P, ctypes.c_int, P, I32, P, P], ctypes.c_int),
             "sw_cache_inspect": ([H, ctypes.POINTER(sw_slot_info), I32, ctypes.POINTER(I32)], ctypes.c_int),
             "sw_cache_read_slot": ([H, I32, ctypes.c_int, P, P], ctypes.c_int),
@@ -80,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "sw_graph_launch": ([H, P], ctypes.c_int),
             "sw_graph_destroy": ([H], ctypes.c_int),
             "sw_cache_ring_period": ([H, ctypes.POINTER(I32)], ctypes.c_int),
+            "sw_probe_mfma": ([P, ctypes.c_int, I32, P, I32, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -153,9 +156,9 @@ def sw_tile_mask_budget(handle: int, keep_frac: float) -> int:
     return k.value
 
 
-def sw_build_tile_mask(handle: int, q_ptr: int, keep_frac: float, out_ptr: int, k_cap: int) -> int:
+def sw_build_tile_mask(handle: int, q_ptr: int, step: int, keep_frac: float, out_ptr: int, k_cap: int) -> int:
     k = ctypes.c_int32()
-    _check(lib().sw_build_tile_mask(handle, q_ptr, keep_frac, out_ptr, k_cap, ctypes.byref(k)),
+    _check(lib().sw_build_tile_mask(handle, q_ptr, step, keep_frac, out_ptr, k_cap, ctypes.byref(k)),
            "sw_build_tile_mask")
     return k.value
 
@@ -201,3 +204,12 @@ def sw_cache_ring_period(handle: int) -> int:
     p = ctypes.c_int32()
     _check(lib().sw_cache_ring_period(handle, ctypes.byref(p)), "sw_cache_ring_period")
     return p.value
+
+
+def sw_probe_mfma(stream_ptr: Optional[int], dtype: int, iters: int, sink_ptr: int, sink_floats: int) -> float:
+    """Enqueue the matrix-core rate probe; returns the launch's flops (time it on the stream)."""
+    f = ctypes.c_double()
+    st = lib().sw_probe_mfma(stream_ptr or None, dtype, iters, sink_ptr, sink_floats, ctypes.byref(f))
+    if st != SW_OK:
+        raise SwError(st, "sw_probe_mfma", "invalid arguments, short sink or launch failure")
+    return f.value

@@ -66,6 +66,7 @@ class Workload:
     policy: str = "s1"     # "s1" (slot relocation) or "relative" (relative-time)
     sigma_range: Tuple[float, float] = (0.3, 0.8)
     rope_theta: float = 10000.0
+    rope_split: Optional[Tuple[int, int, int]] = None   # RoPE pairs (time, height, width); None: default
     tile: int = 128
     frame_pattern: Optional[Tuple[int, ...]] = None   # frames of block b = pattern[b % len]; None: `frames`
     editing: bool = False            # block 0 is the reference, blocks >= 1 carry source frames
@@ -144,9 +145,10 @@ def rng(seed: int, cfg_id: int, chunk: int, step: int, tag: int) -> np.random.Ge
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """fp32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    """fp32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even (finite values:
+    the 32-bit sum below cannot wrap for them)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    b = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return b.astype(np.uint16)
 
 

@@ -26,7 +26,7 @@ def config_for(w: synth.Workload):
                        lat_w=w.lat_w, n_sink=w.n_sink, n_window=w.n_window, twin=w.twin,
                        sparse=w.sparse_keep is not None, dtype="fp8" if w.attn_fp8 else w.dtype,
                        rope_theta=w.rope_theta,
-                       policy=w.policy, tile=w.tile, editing=w.editing)
+                       policy=w.policy, tile=w.tile, editing=w.editing, rope_pairs=w.rope_split)
 
 
 def to_dev(w: synth.Workload, stored: np.ndarray, device="cuda"):

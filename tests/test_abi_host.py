@@ -170,3 +170,26 @@ def test_mask_budget_matches_oracle():
         if n >= 4:
             c.evict()
         c.append("clean", None, None, n)
+
+
+def test_rope_split_validation():
+    """rope_pairs_t/h/w: zeros give the default split; a given split sizes the tables; a split that
+    does not cover d/2 pairs is rejected, as is one the bf16 / fp8 kernels cannot re-rotate."""
+    import dataclasses
+    w = synth.WORKLOADS[2]
+    base = config_for(w)
+    assert native.sw_cache_required_bytes(dataclasses.replace(base, rope_pairs=(22, 21, 21)).to_c()) == \
+        native.sw_cache_required_bytes(base.to_c())
+    slot = 24 * 6144 * 128 * 2
+    work = 1024 * 256 * 128 * 4 + 1024 * 256 * 4
+    table = 2 * (15 * 16 + 34 * 24 + 60 * 24) * 4
+    got = native.sw_cache_required_bytes(dataclasses.replace(base, rope_pairs=(16, 24, 24)).to_c())
+    assert got == 5 * 2 * slot + ((table + 255) // 256) * 256 + work
+    for bad, status in [((22, 21, 20), native.SW_ERR_INVALID_ARG), ((-1, 33, 32), native.SW_ERR_INVALID_ARG),
+                        ((25, 20, 19), native.SW_ERR_UNSUPPORTED)]:
+        with pytest.raises(native.SwError) as e:
+            native.sw_cache_required_bytes(dataclasses.replace(base, rope_pairs=bad).to_c())
+        assert e.value.status == status, bad
+    # fp32 re-rotates every pair per slot: any split is built
+    f32 = dataclasses.replace(config_for(synth.WORKLOADS[1]), head_dim=128, rope_pairs=(40, 12, 12))
+    assert native.sw_cache_required_bytes(f32.to_c()) > 0

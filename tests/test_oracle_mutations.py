@@ -42,7 +42,7 @@ def test_flipped_rotation_sign_is_caught(monkeypatch):
 
 def test_swapped_axis_split_is_caught(monkeypatch):
     orig = rope.axis_split
-    monkeypatch.setattr(rope, "axis_split", lambda d: tuple(orig(d)[i] for i in (1, 0, 2)))
+    monkeypatch.setattr(rope, "axis_split", lambda d, split=None: tuple(orig(d, split)[i] for i in (1, 0, 2)))
     with pytest.raises(AssertionError):
         _bruteforce_pin(C1)
 

@@ -102,3 +102,15 @@ def test_relocation_closed_forms(S, W, F):
             assert all(-S * F <= t < (S + W + 1) * F for t in s1 + rel)
     with pytest.raises(ValueError):
         rope.relocation_bases("absolute", 1, 1, F)
+
+
+def test_worked_example_custom_split():
+    """A caller-given split (2, 0, 2) at d = 8, theta = 100: no pair follows the row."""
+    g = _load_golden("rope_d8_custom_split.txt")
+    x, pos, expected, params = g[0], g[1], g[2], g[3]
+    theta, split = params[0], tuple(int(v) for v in params[1:])
+    got = rope.rotate(x, rope.angles(pos[0], pos[1], pos[2], 8, theta, split))
+    np.testing.assert_allclose(got, expected, atol=1e-15)
+    assert rope.axis_split(8, split) == (2, 0, 2)
+    with pytest.raises(ValueError):
+        rope.axis_split(8, (2, 1, 2))      # does not cover the 4 pairs

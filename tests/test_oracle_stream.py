@@ -38,6 +38,8 @@ def test_c1_all_chunks_equal_bruteforce():
     dict(n_sink=2, n_window=0),
     dict(twin=True, n_steps=2, dtype="bf16", scale=0.5),
     dict(lat_h=5, lat_w=7, frames=2, head_dim=128, n_heads=2, dtype="bf16", scale=0.5),
+    dict(rope_split=(8, 12, 12)),                     # a caller-given RoPE split (d = 64)
+    dict(rope_split=(20, 0, 12), policy="relative"),  # no pair follows the row
 ])
 def test_variants_equal_bruteforce(variant):
     w = synth.tiny(1, **{**dict(n_heads=2, lat_h=4, lat_w=6, n_chunks=7), **variant})
