@@ -1,22 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of streaming block-causal chunk attention on one MI355X.
 
-A step is one chunk of a 540p (or 720p) stream in steady state (full window,
-eviction every chunk): for each of the 4 denoising steps, append the current
-block's K/V (fused RoPE + append kernel) and attend its queries over
-[sink, 3 window blocks, current] (bf16 MFMA attention kernel); then evict the
-oldest window block and commit the current one (index remaps).  Workload
-variants: TwinCache, 720p relative time, block-sparse (tile mask + sparse
-kernel), variable-length blocks, and frame-aligned editing (the chunk's source
-frames staged once, each query also sees its own instant's source frame).
-Inputs are seeded synthetic N(0,1)*0.5 bf16 tensors of the workload's shapes,
-resident in HBM before timing.
+A step is one chunk of a stream in steady state (full window, eviction every
+chunk): for each denoising step, append the current block's K/V (fused RoPE +
+append kernel) and attend its queries over [sinks, window blocks, current]
+(bf16 MFMA attention kernel); then evict the oldest window block and commit the
+current one (index remaps).  The headline workload is the largest config, the
+720p refiner-style stream (10800 query tokens against 43200 keys, 24 heads,
+relative-time RoPE, one step per chunk); the 540p dense stream (6120 against
+30600, 4 steps per chunk) is timed after it and reported under `also`.  Other
+workloads: TwinCache, block-sparse (tile mask + sparse kernel), variable-length
+blocks, frame-aligned editing, fp8.  Inputs are seeded synthetic N(0,1)*0.5
+bf16 tensors of the workload's shapes, resident in HBM before timing.
 
 Prints ONE JSON line.  `value` = attention TFLOP per chunk / wall time per
 chunk (everything in the step counted in the time).  `roofline` is the
 attention kernel alone (HIP events on the launch stream), against the dense
-MFMA peak of its arithmetic type (bf16, or fp8 for the fp8 workload).
-`cpu_baseline` times the fp64 oracle on a bounded sample.
+MFMA peak of its arithmetic type (bf16, or fp8 for the fp8 workload), and
+against the rate the library's matrix-core probe measures on this device.
+`latency_flatness` is the least-squares slope of per-chunk latency over a
+further run of chunks.  `cpu_baseline` times the fp64 oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -90,56 +93,44 @@ def cpu_baseline(w, sample_heads):
             "seconds": dt}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20, help="timed chunks")
-    ap.add_argument("--warmup", type=int, default=3, help="untimed chunks")
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-heads", type=int, default=24,
-                    help="heads in the oracle sample (24 = one whole 540p call, about 15 s on 16 "
-                         "host threads; 0 = skip)")
-    ap.add_argument("--flat-chunks", type=int, default=0, metavar="N",
-                    help="after the timed steps, time N more chunks one by one and report the latency slope")
-    ap.add_argument("--fused-qkv", action="store_true",
-                    help="stage each step from a packed QKV projection output through the fused "
-                         "RMSNorm + RoPE + append epilogue (the attention then reads the normalised q)")
-    ap.add_argument("--graph", action="store_true",
-                    help="after the eager timing, record one chunk graph per ring phase and time their replays")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run device-to-device copies of MIB MiB (scales PMC byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the chunk attention path is single-GPU (its heads are "
-              "independent and would shard across GPUs without any exchange).", file=sys.stderr)
-        sys.exit(2)
-
+def measured_peak(stream, iters=65536):
+    """Sustained matrix-core rate of this device (bf16 and fp8 MFMA chains with register operands,
+    the library's probe), best of three launches timed with events on `stream`."""
     import torch
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
+    from streaming_block_causal_amd import native
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(8 * cus, dtype=torch.float32, device="cuda")
+    out = {}
+    for name, dt in (("bf16", native.SW_BF16), ("fp8", native.SW_FP8)):
+        best = None
         for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
-        return
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            flops = native.sw_probe_mfma(stream.cuda_stream, dt, iters, sink.data_ptr(), sink.numel())
+            e1.record(stream)
+            e1.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        out[name] = {"tflops": flops / (best * 1e-3) / 1e12, "ms": best,
+                     "datasheet_tflops": PEAK_FP8_TFLOPS if name == "fp8" else PEAK_BF16_TFLOPS}
+    return out
+
+
+def run(args, key, stream, flat_chunks, graph, cpu_heads, probe):
+    """Time one workload's chunk step on `stream`; returns its JSON record."""
+    import torch
 
     import synth
     from streaming_block_causal_amd.cache import Cache, CacheConfig
 
-    w = synth.WORKLOADS[WORKLOADS[args.workload]]
+    dev = "cuda"
+    w = synth.WORKLOADS[WORKLOADS[key]]
     cfg = CacheConfig(n_heads=w.n_heads, head_dim=w.head_dim, frames_per_block=w.frames, lat_h=w.lat_h,
                       lat_w=w.lat_w, n_sink=w.n_sink, n_window=w.n_window, twin=w.twin,
                       sparse=w.sparse_keep is not None, dtype="fp8" if w.attn_fp8 else w.dtype,
                       rope_theta=w.rope_theta,
                       policy=w.policy, editing=w.editing)
-    dev = "cuda"
-    torch.cuda.init()
-    # a side stream (the NULL stream cannot be recorded into a graph); torch's own work follows it
-    stream = torch.cuda.Stream()
-    torch.cuda.set_stream(stream)
     cache = Cache(cfg, device=dev, stream=stream)
     B, H, d, T = w.block_tokens, w.n_heads, w.head_dim, w.n_steps
     shape = (B, H, d)
@@ -243,7 +234,8 @@ def main():
                 es.record(stream)
             step = "final" if s == T - 1 else "intermediate"
             if w.sparse_keep is not None:
-                idx, k_row = cache.build_tile_mask(q, w.sparse_keep, out=mask_buf["idx"], k_cap=mask_buf["k"])
+                idx, k_row = cache.build_tile_mask(q, w.sparse_keep, out=mask_buf["idx"], k_cap=mask_buf["k"],
+                                                   step=step)
                 last_mask["idx"] = idx
                 if record:
                     em.record(stream)
@@ -299,15 +291,15 @@ def main():
                   "bytes_moved": 0}
 
     flat = None
-    if args.flat_chunks > 0:
+    if flat_chunks > 0:
         # per-chunk latency over a long steady stream: least-squares slope vs chunk index
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.flat_chunks + 1)]
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(flat_chunks + 1)]
         marks[0].record(stream)
-        for i in range(args.flat_chunks):
+        for i in range(flat_chunks):
             chunk(False)
             marks[i + 1].record(stream)
         torch.cuda.synchronize()
-        lat = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.flat_chunks)]
+        lat = [marks[i].elapsed_time(marks[i + 1]) for i in range(flat_chunks)]
         n = len(lat)
         xm, ym = (n - 1) / 2.0, sum(lat) / n
         slope = sum((i - xm) * (y - ym) for i, y in enumerate(lat)) / max(sum((i - xm) ** 2 for i in range(n)), 1e-30)
@@ -315,7 +307,7 @@ def main():
                 "slope_pct_of_mean_per_100_chunks": 100.0 * slope * 100.0 / ym}
 
     graph_rec = None
-    if args.graph:
+    if graph:
         if w.frame_pattern is not None:
             graph_rec = {"skipped": "block lengths follow a pattern: the ring layout does not repeat"}
         else:
@@ -397,7 +389,7 @@ def main():
         "latency_flatness": flat,
         "cache_host_us": cache_host,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": load_traffic(args.workload),
+                     "frac": achieved / peak, "traffic": load_traffic(key),
                      "kernel": ("attend_fp8_kernel<4>" if w.attn_fp8 else
                                 "attend_bf16_kernel<true, 4, false>" if w.sparse_keep else
                                 "attend_bf16_kernel<false, 8, true>" if w.editing else "attend_bf16_kernel<false, 8, false>"),
@@ -423,10 +415,82 @@ def main():
     if w.editing:
         src_ms = [a.elapsed_time(b) for a, b in ev["source"]]
         res["source_append_ms_per_chunk"] = sum(src_ms) / len(src_ms)
-    if args.cpu_heads > 0:
-        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.n_heads))
+    if probe is not None:
+        mp = probe["fp8" if w.attn_fp8 else "bf16"]["tflops"]
+        res["roofline"]["measured_peak"] = mp
+        res["roofline"]["frac_of_measured_peak"] = achieved / mp
+    if cpu_heads < 0:   # about 2.3 TFLOP of oracle work (one whole 540p call)
+        cpu_heads = max(1, min(w.n_heads, round(w.n_heads * 2.301e12 / flops_call)))
+    if cpu_heads > 0:
+        res["cpu_baseline"] = cpu_baseline(w, min(cpu_heads, w.n_heads))
     else:
         res["cpu_baseline"] = None
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed chunks")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed chunks")
+    ap.add_argument("--workload", default="c4", choices=sorted(WORKLOADS),
+                    help="the headline workload (default: the 720p refiner stream, the largest config)")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads timed after the headline and reported under "
+                         "'also' in the same line (default: c2 when the headline is c4; 'none' = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=-1,
+                    help="heads in the oracle sample (-1 = as many as make about 2.3 TFLOP, i.e. one "
+                         "whole 540p call or 10 heads of a 720p call, about 15 s on 16 host threads; "
+                         "0 = skip)")
+    ap.add_argument("--flat-chunks", type=int, default=200, metavar="N",
+                    help="after the timed steps, time N more chunks one by one and report the latency "
+                         "slope (headline workload only; 0 = skip)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the matrix-core rate probe (measured peak)")
+    ap.add_argument("--fused-qkv", action="store_true",
+                    help="stage each step from a packed QKV projection output through the fused "
+                         "RMSNorm + RoPE + append epilogue (the attention then reads the normalised q)")
+    ap.add_argument("--graph", action="store_true",
+                    help="after the eager timing, record one chunk graph per ring phase and time their replays")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run device-to-device copies of MIB MiB (scales PMC byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the chunk attention path is single-GPU (its heads are "
+              "independent and would shard across GPUs without any exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
+        return
+
+    import synth
+
+    torch.cuda.init()
+    # a side stream (the NULL stream cannot be recorded into a graph); torch's own work follows it
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    probe = None if args.no_probe else measured_peak(stream)
+    res = run(args, args.workload, stream, args.flat_chunks, args.graph, args.cpu_heads, probe)
+    also = args.also if args.also is not None else ("c2" if args.workload == "c4" else "none")
+    if also != "none":
+        res["also"] = {}
+        for key in also.split(","):
+            r = run(args, key, stream, 0, False, 0, probe)
+            res["also"][r["config"]["workload"]] = {
+                k: r[k] for k in ("value", "unit", "ms_per_step", "latent_frames_per_s", "attention_ms_per_call",
+                                  "attention_ms_p50_p95", "append_ms_per_call", "append_gbps", "dtype")}
+            res["also"][r["config"]["workload"]]["roofline"] = r["roofline"]
+    if probe is not None:
+        res["measured_peak"] = probe
     print(json.dumps(res), flush=True)
 
 

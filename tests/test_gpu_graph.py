@@ -5,13 +5,15 @@ step) is captured and replayed (Vidu S2 paper read, section 2.4, the kernel-leve
 In steady state the ring layout repeats every n_window + 1 chunks, so one graph per
 phase, replayed in turn with each chunk's inputs copied into the recorded buffers,
 continues the stream.  Every replay is compared bit for bit with an eager cache fed
-the same inputs, with eager work and synchronisations between replays.
+the same inputs, with eager work and synchronisations between replays, and the last
+replayed chunk with the fp64 oracle.
 """
 import pytest
 
 import synth
+from oracle import stream as ostream
 
-from .helpers import config_for, to_dev, window_len_after
+from .helpers import compare, config_for, to_dev, to_f64, window_len_after
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +68,7 @@ def test_graph_replay_equals_eager(kind):
                 c.append("source", ks, vs, n)
             step = "final" if s == T - 1 else "intermediate"
             if idx is not None and n >= first:   # block-sparse in steady state (fixed budget)
-                _, kr = c.build_tile_mask(q[s], w.sparse_keep, out=idx, k_cap=state["k_row"])
+                _, kr = c.build_tile_mask(q[s], w.sparse_keep, out=idx, k_cap=state["k_row"], step=step)
                 assert kr == state["k_row"]
                 c.attend(q[s], step, tile_idx=idx, k_row=kr, out=out[s])
             else:
@@ -128,5 +130,19 @@ def test_graph_replay_equals_eager(kind):
         for s in range(T):
             assert torch.equal(so[s], ref[s]), (kind, n, s)
         print(f"  chunk {n} phase {(n - first) % period}: equal", flush=True)
+    # the last replayed chunk against the fp64 oracle, every row of every step (block-sparse: the
+    # final step, on the mask the replay built -- it holds that step's mask, and may differ from
+    # the oracle's own only at near-ties)
+    kept, steps = None, range(T)
+    if kind == "sparse":
+        g = sidx.cpu().numpy()
+        kept = [[[int(x) for x in row if x >= 0] for row in g[h]] for h in range(w.n_heads)]
+        steps = [T - 1]
+    st = ostream.Stream(w)
+    for s in steps:
+        ref, _, _ = st.call(n, s + 1, kept=kept)
+        ok, m = compare(to_f64(so[s]), ref, "fp8" if w.attn_fp8 else w.dtype)
+        print(f"  chunk {n} step {s + 1} vs oracle: {m}", flush=True)
+        assert ok, (kind, n, s, m)
     for g in graphs:
         g.close()
