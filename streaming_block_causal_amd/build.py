@@ -42,9 +42,36 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BUILD) -> str:
     """Compile and link; `defines` are extra -D flags (tuning variants), `out` the library path."""
+    objs = _compile(SOURCES, verbose, defines, build_dir)
+    tmp = out + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, out)
+    return out
+
+
+def build_sanitized(build_dir: str = os.path.join(BUILD, "asan"), verbose: bool = False) -> str:
+    """The library with its host code (host.cpp: cache bookkeeping, argument checks, dispatch)
+    compiled by g++ with AddressSanitizer and UndefinedBehaviorSanitizer; the kernels as in
+    build().  Returns the library path.  Load it with SWATTN_LIB=<path> and the ASan runtime
+    preloaded (LD_PRELOAD=$(gcc -print-file-name=libasan.so)); the device code is not
+    instrumented."""
+    objs = _compile([x for x in SOURCES if x.endswith(".hip")], verbose, (), build_dir)
+    host = os.path.join(build_dir, "host_sanitized.o")
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
+    _run(["g++", "-O1", "-g", "-fPIC", "-std=c++17", *san, "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+          "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, "host.cpp"), "-o", host], verbose)
+    out = os.path.join(build_dir, "libswattn.so")
+    _run(["g++", "-shared", *san, "-o", out + ".tmp", host, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+          "-Wl,-rpath,/opt/rocm/lib"], verbose)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _compile(sources, verbose, defines, build_dir):
+    """hipcc -c of each source (in parallel) into build_dir; returns the object paths."""
     os.makedirs(build_dir, exist_ok=True)
     objs, procs = [], []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
@@ -63,10 +90,7 @@ def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BU
             print(err, file=sys.stderr)
     if failed:
         raise RuntimeError("HIP build failed:\n" + "\n\n".join(failed))
-    tmp = out + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, out)
-    return out
+    return objs
 
 
 if __name__ == "__main__":

@@ -13,7 +13,8 @@ import re
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libswattn.so")
+# SWATTN_LIB: another build of the same library (the sanitizer build of the host code)
+LIB_PATH = os.environ.get("SWATTN_LIB") or os.path.join(HERE, "libswattn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "swattn.h")
 
 SW_OK, SW_ERR_INVALID_ARG, SW_ERR_SHAPE, SW_ERR_STATE, SW_ERR_CAPACITY, SW_ERR_UNSUPPORTED, SW_ERR_HIP = range(7)
