@@ -25,8 +25,11 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* sink)
     v8i a, b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      a[i] = 0x38383838 ^ (lane & 7);   // E4M3 values near 1
-      b[i] = 0x30303030 ^ (lane & 3);
+      // scattered finite E4M3 bytes (exponent field <= 14), as varied as real data: a constant
+      // operand toggles fewer bits and lets the clock run higher than attention ever sees
+      const uint32_t ha = (uint32_t)(lane * 8 + i + 1) * 2654435761u, hb = (uint32_t)(lane * 8 + i + 7) * 2246822519u;
+      a[i] = (int)((ha ^ (ha >> 15)) & 0x77777777u);
+      b[i] = (int)((hb ^ (hb >> 13)) & 0x77777777u);
     }
     for (int it = 0; it < iters; ++it) {
       c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 0, 0, 0, 127, 0, 127);
@@ -37,7 +40,7 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* sink)
   } else {
     bf16x8 a, b;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i) {   // varied values (see the fp8 operands)
       a[i] = (__bf16)(x * (float)(i + 1));
       b[i] = (__bf16)(x - 0.01f * (float)i);
     }
