@@ -243,6 +243,24 @@ sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, sw_step_kind step, 
 sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step,
                           const int32_t* tile_idx, int32_t k_row, void* out, float* lse_out);
 
+/* sw_chunk_attend for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, same work split and the same result bit for bit; the only scratch
+ * memory of the attention -- the partial outputs and sum-exps of the query tiles
+ * the dense launch cuts into key ranges -- lives in a static device array of the
+ * library instead of the cache pool's workspace: 65536 rows of 128 + 1 floats
+ * (33.8 MB) per GPU, held by each GPU the library runs on until the process
+ * ends.  Allocates nothing; the first call on a device looks the array up
+ * (hipGetSymbolAddress) once.  The array needs no clearing (every partial row is
+ * written before the merge reads it).  Every call on one GPU shares the array,
+ * which keeps the last call's contents: calls that overlap on one GPU (several
+ * streams or threads) race.  SW_ERR_CAPACITY, with a message, when the call's
+ * split needs more rows than the array holds (fewer query tiles than the device
+ * has compute units, e.g. 1-frame 540p blocks: use sw_chunk_attend); every other
+ * error as sw_chunk_attend. */
+sw_status sw_chunk_attend_noalloc(sw_cache* c, const void* q_raw, sw_step_kind step,
+                                  const int32_t* tile_idx, int32_t k_row, void* out, float* lse_out);
+
 /* Logical slots in attention order (sinks, window oldest->newest, staged
  * current).  Writes min(cap, count) entries; *n = count. Host-only. */
 sw_status sw_cache_inspect(const sw_cache* c, sw_slot_info* out, int32_t cap, int32_t* n);

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libswattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["host.cpp", "append.hip", "append_fp8.hip", "attend.hip", "tilemask.hip", "probe.hip"]
+SOURCES = ["host.cpp", "append.hip", "append_fp8.hip", "attend.hip", "tilemask.hip", "probe.hip", "noalloc.hip"]
 # attention: scores are finite or -inf, so max/min need no NaN canonicalisation (v_max3)
 EXTRA = {"attend.hip": ["-fno-honor-nans"]}
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",

@@ -1178,6 +1178,21 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
   return hipGetLastError();
 }
 
+// Rows of partial results the dense bf16 or fp8 launch of these slots writes to the split
+// workspace under `plan` (the same planning as the launches below; 0 when nothing is split).
+int split_rows(const Geometry& g, bool fp8, const SlotPtrs* slots, int n_slots, const SplitPlan& plan) {
+  if (n_slots < 1 || n_slots > kMaxSlots) return 0;
+  AttnArgs a;
+  const int NW = fp8 ? kFp8Waves : kDenseWaves, ROWS = 32 * NW;
+  a.n_qt = (g.B + ROWS - 1) / ROWS;
+  int blocks = 0;
+  for (int l = 0; l < n_slots; ++l)
+    if (!slots[l].aligned) blocks += (slots[l].count + KB - 1) / KB;
+  const int conc = NW == 4 ? 2 * plan.cus : plan.cus;
+  const int tail = plan_split(a, plan, a.n_qt * g.H, conc, ROWS, blocks);
+  return tail * a.n_split * ROWS;
+}
+
 hipError_t launch_attend_fp8(const Geometry& g, const RopeTab& rt, const void* q, const SlotPtrs* slots, int n_slots,
                              void* out, float* lse, const SplitPlan& plan, hipStream_t stream) {
   if (n_slots < 1 || n_slots > kMaxSlots || g.d != 128) return hipErrorInvalidValue;

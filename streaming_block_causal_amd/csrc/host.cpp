@@ -189,6 +189,7 @@ struct sw_cache {
   sw_rope_policy policy;
   SplitPlan plan;
   bool capturing;      // between sw_graph_begin and sw_graph_end
+  int dev;             // the device current at create
 };
 
 struct sw_graph {
@@ -284,6 +285,84 @@ sw_status write_block(sw_cache* c, const void* k, const void* v, char* kd, char*
 
 }  // namespace
 
+namespace {
+
+// One denoising step's attention (sw_chunk_attend).  part_o == nullptr: the split workspace of
+// the cache pool; otherwise the caller's workspace of max_rows rows, which must hold the split the
+// pool's plan makes (so that both give the same work split and the same result).
+sw_status chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step, const int32_t* tile_idx, int32_t k_row,
+                       void* out, float* lse_out, float* part_o, float* part_lse, int max_rows) {
+  sw_status st = check_ptr(q_raw, "q_raw");
+  if (st == SW_OK) st = check_ptr(out, "out");
+  if (st != SW_OK) return st;
+  if (step != SW_STEP_INTERMEDIATE && step != SW_STEP_FINAL)
+    return fail(SW_ERR_INVALID_ARG, "unknown step kind %d", (int)step);
+  if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache cannot launch kernels");
+  if (!c->staged) return fail(SW_ERR_STATE, "no staged current block (append SW_KV_CURRENT first)");
+  if (c->noisy_due) return fail(SW_ERR_STATE, "a noisy append is due");
+  if (tile_idx) {
+    if (c->cfg.dtype != SW_BF16) return fail(SW_ERR_UNSUPPORTED, "block-sparse attention needs bf16");
+    if (c->src_staged) return fail(SW_ERR_UNSUPPORTED, "frame-aligned editing attention is dense only");
+    if (k_row < 1) return fail(SW_ERR_INVALID_ARG, "k_row must be >= 1 with a tile list");
+    if (!all_full(c)) return fail(SW_ERR_UNSUPPORTED, "block-sparse attention needs full-length blocks");
+  }
+  const std::vector<Entry> hist = history(c);
+  const std::vector<int> b = bases_of(c);
+  const int n_slots = (int)hist.size() + 1;
+  if (tile_idx && k_row > n_slots * c->L.g.nt)
+    return fail(SW_ERR_INVALID_ARG, "k_row %d exceeds the %d key tiles", k_row, n_slots * c->L.g.nt);
+  const bool noisy = c->cfg.twin && step == SW_STEP_INTERMEDIATE;
+  SlotPtrs slots[kMaxSlots];
+  for (int l = 0; l + 1 < n_slots; ++l) {
+    const int p = hist[l].phys;
+    slots[l] = SlotPtrs{noisy ? c->kn[p] : c->kc[p], noisy ? c->vn[p] : c->vc[p], b.back() - b[l],
+                        tokens_of(c, hist[l].frames), 0};
+  }
+  slots[n_slots - 1] = SlotPtrs{c->kc[c->staging], c->vc[c->staging], 0, tokens_of(c, c->staged_frames), 0};
+  int n_all = n_slots;
+  if (c->src_staged)   // the source frames sit at the current block's positions, frame-aligned
+    slots[n_all++] = SlotPtrs{c->ks, c->vs, 0, tokens_of(c, c->staged_frames), 1};
+  Geometry gq = c->L.g;   // the queries are the staged block's tokens
+  gq.B = tokens_of(c, c->staged_frames);
+  SplitPlan plan = c->plan;
+  if (part_o) {   // the caller's workspace: same plan as the pool's, so it must hold that split
+    const int need = (tile_idx || c->cfg.dtype == SW_F32)
+                         ? 0 : split_rows(gq, c->cfg.dtype == SW_FP8, slots, n_all, c->plan);
+    if (need > max_rows)
+      return fail(SW_ERR_CAPACITY,
+                  "this call splits %d query rows into key ranges; the static scratch holds %d (fewer query tiles "
+                  "than compute units: use sw_chunk_attend)", need, max_rows);
+    plan.part_o = part_o;
+    plan.part_lse = part_lse;
+  }
+  const hipError_t e = c->cfg.dtype == SW_FP8
+                            ? launch_attend_fp8(gq, c->rt, q_raw, slots, n_all, out, lse_out, plan, c->stream)
+                            : launch_attend(gq, c->rt, c->cfg.dtype == SW_BF16, q_raw, slots, n_all, tile_idx, k_row,
+                                            out, lse_out, plan, c->stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return SW_OK;
+}
+
+
+}  // namespace
+
+namespace swhost {
+
+int cache_device(const sw_cache* c) { return c->dev; }
+
+int chunk_attend_scratch(sw_cache* c, const void* q_raw, int step, const int32_t* tile_idx, int32_t k_row, void* out,
+                         float* lse_out, float* part_o, float* part_lse, int max_rows) {
+  if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
+  if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache cannot launch kernels");
+  if (!part_o || !part_lse || max_rows < 0) return fail(SW_ERR_INVALID_ARG, "no scratch workspace");
+  return chunk_attend(c, q_raw, static_cast<sw_step_kind>(step), tile_idx, k_row, out, lse_out, part_o, part_lse,
+                      max_rows);
+}
+
+int hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
+
+}  // namespace swhost
+
 extern "C" {
 
 const char* sw_last_error(void) { return g_err.c_str(); }
@@ -353,6 +432,7 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
       return hip_fail(de, "device query");
     }
     c->plan.cus = cus;
+    c->dev = dev;
     std::vector<float> host;
     fill_tables(L, cfg->rope_theta, host);
     hipError_t e = hipMemsetAsync(c->pool, 0, L.total, c->stream);
@@ -383,7 +463,10 @@ sw_status sw_cache_create(const sw_cache_config* cfg, void* device_pool, size_t 
   c->noisy_entry = Entry{-1, -1, 0};
   c->src_staged = false;
   c->capturing = false;
-  if (dry) c->ks = c->vs = nullptr;
+  if (dry) {
+    c->ks = c->vs = nullptr;
+    c->dev = -1;
+  }
   c->policy = cfg->policy;
   if (dry) c->plan = SplitPlan{0, 0, nullptr, nullptr};
   *out = c;
@@ -687,44 +770,7 @@ sw_status sw_build_tile_mask(sw_cache* c, const void* q_raw, sw_step_kind step, 
 sw_status sw_chunk_attend(sw_cache* c, const void* q_raw, sw_step_kind step, const int32_t* tile_idx,
                           int32_t k_row, void* out, float* lse_out) {
   if (!c) return fail(SW_ERR_INVALID_ARG, "cache is NULL");
-  sw_status st = check_ptr(q_raw, "q_raw");
-  if (st == SW_OK) st = check_ptr(out, "out");
-  if (st != SW_OK) return st;
-  if (step != SW_STEP_INTERMEDIATE && step != SW_STEP_FINAL)
-    return fail(SW_ERR_INVALID_ARG, "unknown step kind %d", (int)step);
-  if (c->dry) return fail(SW_ERR_STATE, "metadata-only cache cannot launch kernels");
-  if (!c->staged) return fail(SW_ERR_STATE, "no staged current block (append SW_KV_CURRENT first)");
-  if (c->noisy_due) return fail(SW_ERR_STATE, "a noisy append is due");
-  if (tile_idx) {
-    if (c->cfg.dtype != SW_BF16) return fail(SW_ERR_UNSUPPORTED, "block-sparse attention needs bf16");
-    if (c->src_staged) return fail(SW_ERR_UNSUPPORTED, "frame-aligned editing attention is dense only");
-    if (k_row < 1) return fail(SW_ERR_INVALID_ARG, "k_row must be >= 1 with a tile list");
-    if (!all_full(c)) return fail(SW_ERR_UNSUPPORTED, "block-sparse attention needs full-length blocks");
-  }
-  const std::vector<Entry> hist = history(c);
-  const std::vector<int> b = bases_of(c);
-  const int n_slots = (int)hist.size() + 1;
-  if (tile_idx && k_row > n_slots * c->L.g.nt)
-    return fail(SW_ERR_INVALID_ARG, "k_row %d exceeds the %d key tiles", k_row, n_slots * c->L.g.nt);
-  const bool noisy = c->cfg.twin && step == SW_STEP_INTERMEDIATE;
-  SlotPtrs slots[kMaxSlots];
-  for (int l = 0; l + 1 < n_slots; ++l) {
-    const int p = hist[l].phys;
-    slots[l] = SlotPtrs{noisy ? c->kn[p] : c->kc[p], noisy ? c->vn[p] : c->vc[p], b.back() - b[l],
-                        tokens_of(c, hist[l].frames), 0};
-  }
-  slots[n_slots - 1] = SlotPtrs{c->kc[c->staging], c->vc[c->staging], 0, tokens_of(c, c->staged_frames), 0};
-  int n_all = n_slots;
-  if (c->src_staged)   // the source frames sit at the current block's positions, frame-aligned
-    slots[n_all++] = SlotPtrs{c->ks, c->vs, 0, tokens_of(c, c->staged_frames), 1};
-  Geometry gq = c->L.g;   // the queries are the staged block's tokens
-  gq.B = tokens_of(c, c->staged_frames);
-  const hipError_t e = c->cfg.dtype == SW_FP8
-                            ? launch_attend_fp8(gq, c->rt, q_raw, slots, n_all, out, lse_out, c->plan, c->stream)
-                            : launch_attend(gq, c->rt, c->cfg.dtype == SW_BF16, q_raw, slots, n_all, tile_idx, k_row,
-                                            out, lse_out, c->plan, c->stream);
-  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-  return SW_OK;
+  return chunk_attend(c, q_raw, step, tile_idx, k_row, out, lse_out, nullptr, nullptr, 0);
 }
 
 sw_status sw_cache_inspect(const sw_cache* c, sw_slot_info* out, int32_t cap, int32_t* n) {

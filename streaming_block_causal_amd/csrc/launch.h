@@ -70,6 +70,10 @@ hipError_t launch_attend(const Geometry& g, const RopeTab& rt, bool bf16, const 
                          const SlotPtrs* slots, int n_slots, const int32_t* tile_idx, int k_row,
                          void* out, float* lse, const SplitPlan& plan, hipStream_t stream);
 
+// Rows of the split workspace the dense bf16 (fp8 = false) or fp8 attention launch over these
+// slots uses under `plan` (0 when no tile is split).
+int split_rows(const Geometry& g, bool fp8, const SlotPtrs* slots, int n_slots, const SplitPlan& plan);
+
 // fp8 caches (d = 128): K1 quantising K (after block-local RoPE) and V to E4M3 with power-of-two
 // scales per 32 values (layout: append_fp8.hip); the fp8 attention (dense, bf16 queries and
 // output); the read-back, dequantised to fp32 [B][H][d].
@@ -90,3 +94,17 @@ hipError_t launch_unpack(const Geometry& g, bool bf16, const void* k_src, const 
                          void* k_out, void* v_out, hipStream_t stream);
 
 }  // namespace swattn
+
+// Host-library internals used by the allocation-free attention entry point (host.cpp).
+struct sw_cache;
+namespace swhost {
+// The device the cache was created on.
+int cache_device(const sw_cache* c);
+// sw_chunk_attend with the split workspace at (part_o [max_rows][128], part_lse [max_rows])
+// instead of the cache pool's: the same work split as sw_chunk_attend, and SW_ERR_CAPACITY when
+// it needs more than max_rows rows.  Returns an sw_status.
+int chunk_attend_scratch(sw_cache* c, const void* q_raw, int step, const int32_t* tile_idx, int32_t k_row, void* out,
+                         float* lse_out, float* part_o, float* part_lse, int max_rows);
+// Record a failed HIP call as the thread's last error; returns SW_ERR_HIP.
+int hip_error(hipError_t e, const char* what);
+}  // namespace swhost

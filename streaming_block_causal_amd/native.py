@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
             "sw_tile_mask_budget": ([H, F32, ctypes.POINTER(I32)], ctypes.c_int),
             "sw_build_tile_mask": ([H, P, ctypes.c_int, F32, P, I32, ctypes.POINTER(I32)], ctypes.c_int),
             "sw_chunk_attend": ([H, P, ctypes.c_int, P, I32, P, P], ctypes.c_int),
+            "sw_chunk_attend_noalloc": ([H, P, ctypes.c_int, P, I32, P, P], ctypes.c_int),
             "sw_cache_inspect": ([H, ctypes.POINTER(sw_slot_info), I32, ctypes.POINTER(I32)], ctypes.c_int),
             "sw_cache_read_slot": ([H, I32, ctypes.c_int, P, P], ctypes.c_int),
             "sw_graph_begin": ([H], ctypes.c_int),
@@ -168,6 +169,12 @@ def sw_chunk_attend(handle: int, q_ptr: int, step: int, tile_ptr: Optional[int],
                     lse_ptr: Optional[int]) -> None:
     _check(lib().sw_chunk_attend(handle, q_ptr, step, tile_ptr or None, k_row, out_ptr, lse_ptr or None),
            "sw_chunk_attend")
+
+
+def sw_chunk_attend_noalloc(handle: int, q_ptr: int, step: int, tile_ptr: Optional[int], k_row: int, out_ptr: int,
+                            lse_ptr: Optional[int]) -> None:
+    _check(lib().sw_chunk_attend_noalloc(handle, q_ptr, step, tile_ptr or None, k_row, out_ptr, lse_ptr or None),
+           "sw_chunk_attend_noalloc")
 
 
 def sw_cache_inspect(handle: int, cap: int = 16):
