@@ -21,7 +21,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/swattn.h"
+#include "swattn.h"
 #include "launch.h"
 
 using namespace swattn;

@@ -10,7 +10,7 @@
 
 #include <mutex>
 
-#include "../../include/swattn.h"
+#include "swattn.h"
 #include "launch.h"
 
 namespace {

@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/swattn.h"
+#include "swattn.h"
 #include "device_common.h"
 
 namespace swattn {
