@@ -73,6 +73,18 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Largest of a lane's 32 scores (two 32x32 score tiles): a tree of max3 steps, depth 4, rather
+// than a chain of 16 dependent ones.
+__device__ __forceinline__ float max_of_32(const f32x16& s0, const f32x16& s1) {
+  float m8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m8[i] = fmaxf(fmaxf(s0[2 * i], s0[2 * i + 1]), s1[2 * i]);
+  const float a = fmaxf(fmaxf(m8[0], m8[1]), m8[2]), b = fmaxf(fmaxf(m8[3], m8[4]), m8[5]);
+  const float c = fmaxf(fmaxf(m8[6], m8[7]), s1[1]), d = fmaxf(fmaxf(s1[3], s1[5]), s1[7]);
+  const float e = fmaxf(fmaxf(s1[9], s1[11]), s1[13]);
+  return fmaxf(fmaxf(a, b), fmaxf(fmaxf(c, d), fmaxf(e, s1[15])));
+}
+
 // ------------------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ------------------------------------------------------------------------------------
@@ -354,9 +366,7 @@ void attend_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < PV_AHEAD; ++i) vop[i] = vread(i);
     __builtin_amdgcn_sched_barrier(0);
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    float mx = max_of_32(s0, s1);
     mx = swap_halves_max(mx) * scale_log2;
     if (__any(mx > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mx);
@@ -908,9 +918,7 @@ void attend_fp8_kernel(AttnArgs a) {
       const u32x4 hi = *reinterpret_cast<const u32x4*>(vl + 2048 * t + voff[1]);
       vop[t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    float mx = max_of_32(s0, s1);
     mx = swap_halves_max(mx) * scale_log2;
     if (__any(mx > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mx);

@@ -120,3 +120,41 @@ def test_planted_unquantised_operand_fails(monkeypatch, which):
         monkeypatch.setattr(fp8, "quantize_v", lambda v: np.asarray(v, dtype=np.float64))
     o_bad, _, _ = ostream.Stream(W).call(4, 1)
     assert not np.allclose(o_bad, o_ref, atol=1e-9)
+
+
+def _plain_fp8(x):
+    """The plain definition of fp8 attention operands: the whole tensor scaled by amax / 448 and
+    rounded to E4M3 by torch's float8_e4m3fn conversion (a library routine), read back."""
+    s = np.abs(x).max() / 448.0
+    return torch.from_numpy((x / s).astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy() * s
+
+
+def test_scheme_agrees_with_plain_per_tensor_fp8():
+    """Against an fp8 attention written from the plain definition -- Q rotated at its relocated
+    positions, K at its slot's relocated positions and V, each quantised with one scale per head
+    -- the oracle's scheme (K quantised at block-local positions, Q per slot, 32-value groups) is
+    no less accurate, and the two differ by about their independent rounding errors added in
+    quadrature (E4M3 keeps 3 mantissa bits: about 3% relative error on the output here)."""
+    exact = ostream.Stream(W.replace(attn_fp8=False))
+    q8 = ostream.Stream(W)
+    for n in (2, 5):
+        o8, _, _ = q8.call(n, 1)
+        oe, _, _ = exact.call(n, 1)
+        q, slots = exact.slot_inputs(n, 1)
+        bases = exact.bases(n)
+        op = np.empty_like(oe)
+        for h in range(W.n_heads):
+            qr = _plain_fp8(ostream.relocated_head(W, q, h, bases[-1]))
+            kr = _plain_fp8(np.concatenate([ostream.relocated_head(W, k, h, bases[l])
+                                            for l, (_, _, k, _) in enumerate(slots)]))
+            vr = _plain_fp8(np.concatenate([synth.as_f64(W, v[:, h, :]) for (_, _, _, v) in slots]))
+            sc = qr @ kr.T / np.sqrt(W.head_dim)
+            e = np.exp(sc - sc.max(axis=1, keepdims=True))
+            op[:, h] = (e @ vr) / e.sum(axis=1, keepdims=True)
+
+        def rel(a, b):
+            return np.linalg.norm(a - b) / np.linalg.norm(b)
+        e_or, e_pl, d = rel(o8, oe), rel(op, oe), rel(o8, op)
+        assert 1e-3 < e_pl < 5e-2, e_pl
+        assert e_or <= 1.25 * e_pl, (e_or, e_pl)
+        assert d <= 1.6 * max(e_or, e_pl), (d, e_or, e_pl)
