@@ -33,6 +33,7 @@ struct MaskArgs {
   int B, H, nt, hw, lat_w;
   int n_slots, has_sink;
   float inv_sqrt_d;
+  float inv_hw, inv_lat_w;   // 1 / (lat_h * lat_w), 1 / lat_w in fp32 (positions by multiplication)
   RopeTab rt;
   const float* pooled[kMaxSlots];
   int delta[kMaxSlots];
@@ -71,32 +72,56 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   const RopeTab rt = a.rt;
 
   // 1. per query tile, the sum over its valid queries of q rotated at block-local positions.
-  //    Thread t takes 4 pairs (16 bytes) of 8 rows of every tile; all loads are issued first.
+  //    Thread t takes 4 pairs (16 bytes) of 8 rows (16 apart) of every tile.  Positions come from
+  //    reciprocal multiplications (exact below 2^16 tokens), and every Q load and every cos/sin
+  //    gather of the thread is issued before the first is used: rows past the block read row 0
+  //    and are dropped by a select, so no branch splits the loads into dependent groups.
   {
     const int pg = tid & 15, rg = tid >> 4;   // pair group (4 pairs), row group
-    uint4 raw[kQT][8];
+    // the axis, row stride and first entry of each of the thread's 4 pairs (fixed for all its
+    // rows); the three tables lie back to back, so one uniform base and 32-bit indices address them
+    const CosSin* tab = rt.t;
+    const int h0 = (int)(rt.h - rt.t), w0 = (int)(rt.w - rt.t);
+    int axis[4], stride[4], col[4];
 #pragma unroll
-    for (int t = 0; t < kQT; ++t)
+    for (int e = 0; e < 4; ++e) {
+      const int p = 4 * pg + e;
+      axis[e] = p < rt.pt ? 0 : (p < rt.pt + rt.ph ? 1 : 2);
+      stride[e] = axis[e] == 0 ? rt.pt : (axis[e] == 1 ? rt.ph : rt.pw);
+      col[e] = axis[e] == 0 ? p : (axis[e] == 1 ? h0 + p - rt.pt : w0 + p - rt.pt - rt.ph);
+    }
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) {
+      uint4 raw[8];
+      CosSin cs[8][4];
+      bool ok[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = (qt0 + t) * kTile + rg + 16 * i;
-        raw[t][i] = (t < n_qt && r < a.B) ? ldg16(a.q + ((size_t)r * a.H + h) * D + 8 * pg) : make_uint4(0, 0, 0, 0);
-      }
+        ok[i] = t < n_qt && r < a.B;
+        const int rr = ok[i] ? r : 0;
+        raw[i] = ldg16(a.q + ((size_t)rr * a.H + h) * D + 8 * pg);
+        const int f = (int)(((float)rr + 0.5f) * a.inv_hw);
+        const int rem = rr - f * a.hw;
+        const int hh = (int)(((float)rem + 0.5f) * a.inv_lat_w);
+        const int ww = rem - hh * a.lat_w;
 #pragma unroll
-    for (int t = 0; t < kQT; ++t) {
+        for (int e = 0; e < 4; ++e) {
+          const int pos = axis[e] == 0 ? f : (axis[e] == 1 ? hh : ww);
+          cs[i][e] = tab[pos * stride[e] + col[e]];
+        }
+      }
       float acc8[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int r = (qt0 + t) * kTile + rg + 16 * i;
-        if (t >= n_qt || r >= a.B) continue;
-        const int f = r / a.hw, rem = r - f * a.hw, hh = rem / a.lat_w, ww = rem - hh * a.lat_w;
-        const uint32_t w[4] = {raw[t][i].x, raw[t][i].y, raw[t][i].z, raw[t][i].w};
+        // a row past the block contributes zeros (its loaded row-0 values are dropped)
+        const uint32_t w[4] = {ok[i] ? raw[i].x : 0u, ok[i] ? raw[i].y : 0u, ok[i] ? raw[i].z : 0u,
+                               ok[i] ? raw[i].w : 0u};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float c, sn;
-          rope_cs(rt, 4 * pg + e, f, hh, ww, c, sn);
+          const float c = cs[i][e].c, sn = cs[i][e].s;
           const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xffff0000u);
           acc8[2 * e] += x0 * c - x1 * sn;
           acc8[2 * e + 1] += x0 * sn + x1 * c;
@@ -143,9 +168,13 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   const int f_sink = a.has_sink ? 0 : -1;
   const int f_diag0 = (a.n_slots - 1) * a.nt + qt0;
   for (int u = tid; u < n_kv64; u += 256) {
-    float dot[kQT];
+    // four partial sums over interleaved dimensions: four dependent chains of 32 FMAs instead of
+    // one of 128
+    float dot[kQT][4];
 #pragma unroll
-    for (int t = 0; t < kQT; ++t) dot[t] = 0.f;
+    for (int t = 0; t < kQT; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dot[t][c] = 0.f;
     if (u < n_kv) {
       const int sl = u / a.nt, jt = u - sl * a.nt;
       const float* kp = spooled[sl] + (size_t)h * D * a.nt + jt;
@@ -154,13 +183,14 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
       for (int i = 0; i < D; ++i) {
         const float kv = kp[(size_t)i * a.nt];
 #pragma unroll
-        for (int t = 0; t < kQT; ++t) dot[t] = fmaf(qp[t * a.n_slots * D + i], kv, dot[t]);
+        for (int t = 0; t < kQT; ++t) dot[t][i & 3] = fmaf(qp[t * a.n_slots * D + i], kv, dot[t][i & 3]);
       }
     }
 #pragma unroll
     for (int t = 0; t < kQT; ++t) {
       const bool cand = u < n_kv && u != f_sink && u != f_diag0 + t;
-      keys[t * n_kv64 + u] = cand ? score_key(dot[t] * a.inv_sqrt_d) : 0u;
+      const float d = (dot[t][0] + dot[t][1]) + (dot[t][2] + dot[t][3]);
+      keys[t * n_kv64 + u] = cand ? score_key(d * a.inv_sqrt_d) : 0u;
     }
   }
   __syncthreads();
@@ -245,6 +275,8 @@ hipError_t launch_tile_mask(const Geometry& g, const RopeTab& rt, const void* q,
   a.n_slots = n_slots;
   a.has_sink = has_sink ? 1 : 0;
   a.inv_sqrt_d = (float)(1.0 / __builtin_sqrt((double)g.d));
+  a.inv_hw = 1.0f / (float)(g.lat_h * g.lat_w);
+  a.inv_lat_w = 1.0f / (float)g.lat_w;
   a.rt = rt;
   for (int i = 0; i < kMaxSlots; ++i) {
     a.pooled[i] = i < n_slots ? pooled[i] : nullptr;
