@@ -193,3 +193,22 @@ def test_rope_split_validation():
     # fp32 re-rotates every pair per slot: any split is built
     f32 = dataclasses.replace(config_for(synth.WORKLOADS[1]), head_dim=128, rope_pairs=(40, 12, 12))
     assert native.sw_cache_required_bytes(f32.to_c()) > 0
+
+
+def test_noalloc_and_probe_error_paths():
+    """Host-side checks of the allocation-free attention and the probe (no GPU touched): a
+    metadata-only cache cannot launch; the probe rejects bad arguments before any device call."""
+    import ctypes
+    c = Cache(config_for(synth.WORKLOADS[2]), device=None)
+    c.append("current", 1, 1, 0)
+    with pytest.raises(native.SwError) as e:
+        native.sw_chunk_attend_noalloc(c.handle, 1, native.SW_STEP_FINAL, None, 0, 1, None)
+    assert e.value.status == native.SW_ERR_STATE
+    with pytest.raises(native.SwError) as e:
+        native.sw_chunk_attend_noalloc(None, 1, native.SW_STEP_FINAL, None, 0, 1, None)
+    assert e.value.status == native.SW_ERR_INVALID_ARG
+    f = ctypes.c_double()
+    L = native.lib()
+    assert L.sw_probe_mfma(None, native.SW_BF16, 0, 1, 4096, ctypes.byref(f)) == native.SW_ERR_INVALID_ARG
+    assert L.sw_probe_mfma(None, native.SW_F32, 16, 1, 4096, ctypes.byref(f)) == native.SW_ERR_INVALID_ARG
+    assert L.sw_probe_mfma(None, native.SW_BF16, 16, None, 4096, ctypes.byref(f)) == native.SW_ERR_INVALID_ARG
