@@ -36,12 +36,15 @@ __device__ __forceinline__ u16 f2bf(float f) {
 // selected and one load is issued, so the loads of several pairs can be in flight together
 // (lanes of one wave often hold pairs of different axes; with a branch per axis every branch's
 // load would be issued and waited for on its own).
+// The three tables lie back to back (time, height, width), so one uniform base and a 32-bit
+// index address them: a per-lane choice of 64-bit table pointers costs twice the registers.
 __device__ __forceinline__ void rope_cs(const RopeTab rt, int p, int t, int h, int w, float& c,
                                         float& s) {
   const bool on_t = p < rt.pt, on_h = p < rt.pt + rt.ph;
-  const CosSin* tab = on_t ? rt.t : (on_h ? rt.h : rt.w);
-  const int idx = on_t ? t * rt.pt + p : (on_h ? h * rt.ph + (p - rt.pt) : w * rt.pw + (p - rt.pt - rt.ph));
-  const CosSin v = tab[idx];
+  const int h0 = (int)(rt.h - rt.t), w0 = (int)(rt.w - rt.t);
+  const int idx = on_t ? t * rt.pt + p
+                       : (on_h ? h0 + h * rt.ph + (p - rt.pt) : w0 + w * rt.pw + (p - rt.pt - rt.ph));
+  const CosSin v = rt.t[idx];
   c = v.c;
   s = v.s;
 }

@@ -16,8 +16,9 @@ struct __attribute__((aligned(8))) CosSin {
   float c, s;
 };
 
-// cos/sin tables (computed on the host in fp64, stored fp32) for the three RoPE axes.
-// time: [t_len][pt], height: [lat_h][ph], width: [lat_w][pw].
+// cos/sin tables (computed on the host in fp64, stored fp32) for the three RoPE axes, back to
+// back in one allocation (h and w follow t): time: [t_len][pt], height: [lat_h][ph], width:
+// [lat_w][pw].
 struct RopeTab {
   const CosSin* t;
   const CosSin* h;
