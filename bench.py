@@ -86,11 +86,13 @@ def cpu_baseline(w, sample_heads):
             model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
     except OSError:
         pass
+    call_s = dt * w.n_heads / sample_heads          # the whole call (heads are independent)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "cpu_model": model, "nproc": os.cpu_count(),
             "sample": f"one steady-state call (chunk {n}, step 1), {sample_heads} of {w.n_heads} heads, "
                       f"all {q.shape[0]} queries x {keys} keys, fp64 numpy; {dt:.1f} s",
-            "seconds": dt}
+            "seconds": dt, "call_seconds": call_s, "chunk_seconds": call_s * w.n_steps,
+            "latent_frames_per_s": w.frames / (call_s * w.n_steps)}
 
 
 def measured_peak(stream, iters=65536):
@@ -484,11 +486,12 @@ def main():
     if also != "none":
         res["also"] = {}
         for key in also.split(","):
-            r = run(args, key, stream, 0, False, 0, probe)
+            r = run(args, key, stream, 0, False, args.cpu_heads, probe)
             res["also"][r["config"]["workload"]] = {
                 k: r[k] for k in ("value", "unit", "ms_per_step", "latent_frames_per_s", "attention_ms_per_call",
                                   "attention_ms_p50_p95", "append_ms_per_call", "append_gbps", "dtype")}
             res["also"][r["config"]["workload"]]["roofline"] = r["roofline"]
+            res["also"][r["config"]["workload"]]["cpu_baseline"] = r["cpu_baseline"]
     if probe is not None:
         res["measured_peak"] = probe
     print(json.dumps(res), flush=True)
