@@ -17,8 +17,10 @@ scaled fp8 matrix instructions of CDNA4 and is defined here step by step:
 * V is quantised per channel and head within each 64-key block, in two groups:
   its first 32 keys and its last 32 keys.
 * Q is quantised for each cache slot separately, after its rotation at the
-  relocated time of that slot (the query carries the relocation), in groups of
-  32 consecutive channels of one query and head.
+  relocated time of that slot (the query carries the relocation) and its
+  multiplication by the softmax scale in base 2, log2(e) / sqrt(d), in groups of
+  32 consecutive channels of one query and head: its products with K are then
+  scores in base-2 units, and the softmax takes powers of two.
 * Scores, softmax and the weighted sum of V are exact (float64) on the
   dequantised values.  (The GPU kernel also rounds the probabilities to E4M3
   before the product with V; that rounding is what the GPU tolerance covers.)
@@ -86,32 +88,39 @@ def key_local(w, stored_k: np.ndarray, head: int, as_f64) -> np.ndarray:
     return quantize_groups(rope.rotate(x, rope.angles(f, hh, ww, w.head_dim, w.rope_theta, w.rope_split)))
 
 
+def score_scale(w) -> float:
+    """The softmax scale in base 2: exp(q.k / sqrt(d)) = 2^(q.k * log2(e) / sqrt(d))."""
+    return float(np.log2(np.e) / np.sqrt(w.head_dim))
+
+
 def query_for_slot(w, stored_q: np.ndarray, head: int, delta: int, as_f64) -> np.ndarray:
     """Dequantised Q [B, d] of one head, rotated at block-local time + delta (the slot's
-    relocation: time base of the current block minus that of the slot), then quantised."""
+    relocation: time base of the current block minus that of the slot), multiplied by the
+    softmax scale in base 2, then quantised."""
     x = as_f64(w, stored_q[:, head, :])
     f, hh, ww = rope.block_grid(stored_q.shape[0] // (w.lat_h * w.lat_w), w.lat_h, w.lat_w)
-    return quantize_groups(rope.rotate(x, rope.angles(f + delta, hh, ww, w.head_dim, w.rope_theta, w.rope_split)))
+    rotated = rope.rotate(x, rope.angles(f + delta, hh, ww, w.head_dim, w.rope_theta, w.rope_split))
+    return quantize_groups(rotated * score_scale(w))
 
 
 def attend_head(w, head: int, q_stored, slots, bases, rows, as_f64, row_block: int = 512):
     """(O [rows, d], LSE [rows]) of one head with fp8-quantised Q, K, V (see the module notes).
 
     slots: [(role, block, K_stored, V_stored)] in logical order, the current block last; bases:
-    their time bases.  The scores against slot l use the queries quantised for that slot."""
+    their time bases.  The scores against slot l use the queries quantised for that slot; they
+    are in base-2 units (the scale is in Q), and the LSE is returned in natural units."""
     rows = np.asarray(rows)
     ks = [key_local(w, k, head, as_f64) for (_, _, k, _) in slots]
     vs = np.concatenate([quantize_v(as_f64(w, v[:, head, :])) for (_, _, _, v) in slots], axis=0)
     qs = [query_for_slot(w, q_stored, head, bases[-1] - bases[l], as_f64)[rows] for l in range(len(slots))]
-    scale = 1.0 / np.sqrt(w.head_dim)
     o = np.empty((rows.size, w.head_dim))
     lse = np.empty(rows.size)
     for r0 in range(0, rows.size, row_block):
         r1 = min(rows.size, r0 + row_block)
-        sc = np.concatenate([(qs[l][r0:r1] @ ks[l].T) * scale for l in range(len(slots))], axis=1)
+        sc = np.concatenate([qs[l][r0:r1] @ ks[l].T for l in range(len(slots))], axis=1)
         m = sc.max(axis=1, keepdims=True)
-        e = np.exp(sc - m)
+        e = np.exp2(sc - m)
         den = e.sum(axis=1, keepdims=True)
         o[r0:r1] = (e @ vs) / den
-        lse[r0:r1] = (m + np.log(den))[:, 0]
+        lse[r0:r1] = ((m + np.log2(den)) * np.log(2.0))[:, 0]
     return o, lse

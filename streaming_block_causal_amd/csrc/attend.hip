@@ -293,8 +293,9 @@ void attend_bf16_kernel(AttnArgs a) {
       kb = 0;
     }
     const SlotPtrs sp = sslot[s];
-    kb_ptr = uniform_ptr(static_cast<const u16*>(sp.k) + h * kstride + (size_t)kb * KB * D);
-    vb_ptr = uniform_ptr(static_cast<const u16*>(sp.v) + h * kstride + (size_t)(kb >> 1) * D * kTile + (kb & 1) * KB);
+    // the slot's base made uniform first: the offsets are scalar, so the sums stay in SGPRs
+    kb_ptr = uniform_ptr(sp.k) + h * kstride + (size_t)kb * KB * D;
+    vb_ptr = uniform_ptr(sp.v) + h * kstride + (size_t)(kb >> 1) * D * kTile + (kb & 1) * KB;
   };
 
   // ---- S^T = K Q^T for 64 keys: two 32x32 tiles, lane holds 16 keys of query ln
@@ -679,7 +680,11 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs a) {
 // fp8 MFMA kernel (dense): Q, K, V in OCP E4M3 with power-of-two scales per 32 values,
 // v_mfma_scale_f32_32x32x64_f8f6f4 (each lane's 32 operand bytes carry that lane's
 // E8M0 scale), fp32 softmax, P rounded to E4M3 (scale 1: p <= 2^8 < 448 under the lazy
-// rescale), fp32 accumulation.  Cache layout: see append_fp8.hip.  Same grid, split and
+// rescale), fp32 accumulation.  Q is quantised with the softmax scale in base 2
+// (log2 e / sqrt d) folded in, and each block's S accumulators start at -m_ref (the running
+// max, 0 while the row has none): the MFMAs then deliver the exponents themselves, and the
+// softmax spends no VALU instruction on scaling and shifting 32 scores per lane and block.
+// Cache layout: see append_fp8.hip.  Same grid, split and
 // pipeline as the bf16 dense kernel; per 64-key block a wave issues 4 + 4 MFMAs (64
 // channels or 64 keys of contraction each) and reads 8 KB of K and 8 KB of V^T from LDS.
 // The scaled MFMA applies the E8M0 scale of lane half 0 to operand bytes 0-15 of both lane
@@ -713,12 +718,13 @@ __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d
 }
 
 // Q operand chunks [C0, C1) of one lane: channels 64c + 16hf + [0, 16) and 64c + 32 + 16hf +
-// [0, 16) of its query, rotated at time frame + delta; each half is quantised with the scale of
+// [0, 16) of its query, rotated at time frame + delta and multiplied by qscale (the softmax
+// scale in base 2); each half is quantised with the scale of
 // its 32-channel group (the two lane halves exchange their partial maxima); byte c of qsc is
 // the scale this lane supplies (group 2c + hf)
 template <int C0, int C1>
 __device__ __forceinline__ void load_q8(const RopeTab rt, const u16* qp, bool valid, int qf, int qh, int qw, int hf,
-                                        int delta, v8i (&q8)[2], uint32_t& qsc) {
+                                        int delta, float qscale, v8i (&q8)[2], uint32_t& qsc) {
   const int t = qf + delta;
 #pragma unroll
   for (int c = C0; c < C1; ++c) {
@@ -738,8 +744,8 @@ __device__ __forceinline__ void load_q8(const RopeTab rt, const u16* qp, bool va
             float cs, sn;
             rope_cs(rt, base / 2 + 4 * u + i, t, qh, qw, cs, sn);
             const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xffff0000u);
-            x[8 * u + 2 * i] = x0 * cs - x1 * sn;
-            x[8 * u + 2 * i + 1] = x0 * sn + x1 * cs;
+            x[8 * u + 2 * i] = (x0 * cs - x1 * sn) * qscale;
+            x[8 * u + 2 * i + 1] = (x0 * sn + x1 * cs) * qscale;
           }
         }
       } else {
@@ -816,7 +822,7 @@ void attend_fp8_kernel(AttnArgs a) {
   float m_run = -3.0e38f, l_run = 0.f;   // finite floor, as in the bf16 kernel
   v8i q8[2];
   uint32_t qsc = 0x7f7f7f7fu;
-  load_q8<0, 2>(rt, qp, qvalid, qf, qh, qw, hf, 0, q8, qsc);
+  load_q8<0, 2>(rt, qp, qvalid, qf, qh, qw, hf, 0, scale_log2, q8, qsc);
 
   // per-lane LDS byte offsets of the operand reads (two 16-byte chunks each).  The LDS serves a
   // 16-byte read for 16 lanes at a time from 64 four-byte banks (256 bytes): rows of 128 bytes
@@ -858,10 +864,8 @@ void attend_fp8_kernel(AttnArgs a) {
   };
   auto stage = [&](int s, int kb, int buf) {
     const SlotPtrs sp = sslot[s];
-    const uint8_t* kg = reinterpret_cast<const uint8_t*>(
-        uniform_ptr(static_cast<const uint8_t*>(sp.k) + h * kstride + (size_t)kb * KB * D));
-    const uint8_t* vg = reinterpret_cast<const uint8_t*>(
-        uniform_ptr(static_cast<const uint8_t*>(sp.v) + h * kstride + (size_t)kb * D * KB));
+    const uint8_t* kg = reinterpret_cast<const uint8_t*>(uniform_ptr(sp.k)) + h * kstride + (size_t)kb * KB * D;
+    const uint8_t* vg = reinterpret_cast<const uint8_t*>(uniform_ptr(sp.v)) + h * kstride + (size_t)kb * D * KB;
 #pragma unroll
     for (int p = 0; p < NSTG; ++p) {
       const int C = NW * p + wave;
@@ -879,11 +883,12 @@ void attend_fp8_kernel(AttnArgs a) {
   // ---- S^T = K Q^T for 64 keys: tiles t = 0, 1 (32 keys each), two channel chunks of 64
   auto qk = [&](const uint8_t* kl, int kvalid, uint32_t k0, uint32_t k1, f32x16& s0, f32x16& s1, bool stage_next,
                 int nsl, int nkb, int nbuf) {
+    // reference the scores of this block are shifted by: the running max, or 0 while it is still
+    // at its floor (a shift by the floor would round the scores away)
+    const float m_ref = m_run < -1.0e37f ? 0.f : m_run;
+    f32x16 negm;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = 0.f;
-      s1[r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
     v8i kop[2][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -893,10 +898,10 @@ void attend_fp8_kernel(AttnArgs a) {
         const u32x4 hi = *reinterpret_cast<const u32x4*>(kl + 4096 * t + koff[c][1]);
         kop[c][t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
-    s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[0][0], q8[0], s0, 0, 0, 0, (int)k0, 0, (int)qsc);
+    s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[0][0], q8[0], negm, 0, 0, 0, (int)k0, 0, (int)qsc);
     // the next block's loads ride along with the MFMAs
     if (stage_next) stage(nsl, nkb, nbuf);
-    s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[0][1], q8[0], s1, 0, 0, 0, (int)k1, 0, (int)qsc);
+    s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[0][1], q8[0], negm, 0, 0, 0, (int)k1, 0, (int)qsc);
     s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[1][0], q8[1], s0, 0, 0, 2, (int)k0, 1, (int)qsc);
     s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[1][1], q8[1], s1, 0, 0, 2, (int)k1, 1, (int)qsc);
     if (__builtin_expect(kvalid < KB, 0)) {   // last block of its slot: keys past its end do not exist
@@ -918,9 +923,13 @@ void attend_fp8_kernel(AttnArgs a) {
       const u32x4 hi = *reinterpret_cast<const u32x4*>(vl + 2048 * t + voff[1]);
       vop[t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
+    // the scores arrive as s * scale - m_ref (base 2); m_ref as in qk
+    const float m_ref = m_run < -1.0e37f ? 0.f : m_run;
     float mx = max_of_32(s0, s1);
-    mx = swap_halves_max(mx) * scale_log2;
-    if (__any(mx > m_run + kRescaleSlack)) {
+    mx = swap_halves_max(mx) + m_ref;
+    float p0[16], p1[16];
+    if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
+      __builtin_amdgcn_sched_barrier(0);
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -929,13 +938,17 @@ void attend_fp8_kernel(AttnArgs a) {
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+      const float sh = m_ref - m_new;   // re-reference the scores to the new max
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] += sh;
+        s1[r] += sh;
+      }
     }
-    const float mneg = -m_run;
-    float p0[16], p1[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, mneg));
-      p1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, mneg));
+      p0[r] = __builtin_amdgcn_exp2f(s0[r]);
+      p1[r] = __builtin_amdgcn_exp2f(s1[r]);
     }
     v8i p8;
 #pragma unroll
@@ -1010,7 +1023,7 @@ void attend_fp8_kernel(AttnArgs a) {
     asm volatile("" ::: "memory");
     if (sl != cur_slot) {
       cur_slot = sl;
-      load_q8<0, 1>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, q8, qsc);
+      load_q8<0, 1>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, scale_log2, q8, qsc);
     }
     const bool has_next = pos[1] < i1;
     const int nsl = has_next ? bsl[1] : 0, nkb = has_next ? bkb[1] : 0;

@@ -112,8 +112,9 @@ def test_planted_unquantised_operand_fails(monkeypatch, which):
         f, hh, ww = rope.block_grid(stored.shape[0] // (w.lat_h * w.lat_w), w.lat_h, w.lat_w)
         return rope.rotate(x, rope.angles(f + delta, hh, ww, w.head_dim, w.rope_theta))
 
-    if which == "q":
-        monkeypatch.setattr(fp8, "query_for_slot", rotated)
+    if which == "q":   # rotated and scaled, not quantised
+        monkeypatch.setattr(fp8, "query_for_slot",
+                            lambda w, q, h, d, as_f64: rotated(w, q, h, d, as_f64) * fp8.score_scale(w))
     elif which == "k":
         monkeypatch.setattr(fp8, "key_local", lambda w, k, h, as_f64: rotated(w, k, h, 0, as_f64))
     else:
