@@ -104,6 +104,7 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units: exp2 arguments stay <= 8 
 // Only the first kTimeJ operand groups hold time pairs (d = 128: 22 time pairs = dims 0..43), so a
 // new slot re-rotates those and the spatial groups are computed once per workgroup.
 constexpr int kTimeJ = 3;
+constexpr int kTimeTabLds = 1024;   // time-table entries the block-sparse kernel copies to LDS
 template <int J0, int J1>
 __device__ __forceinline__ void load_q(const RopeTab rt, const u16* qp, bool valid, int qf, int qh, int qw,
                                        int hf, int delta, bf16x8 (&qb)[8]) {
@@ -124,6 +125,28 @@ __device__ __forceinline__ void load_q(const RopeTab rt, const u16* qp, bool val
       const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xffff0000u);
       qb[j][2 * i] = (__bf16)(x0 * c - x1 * s);
       qb[j][2 * i + 1] = (__bf16)(x0 * s + x1 * c);
+    }
+  }
+}
+
+// Slot entry: the time pairs among the first kTimeJ operand groups re-rotated at time t from the
+// raw query (raw[j]: q[16j + 8hf .. +8) as loaded, zero for rows past the block); the other pairs
+// of these groups keep the values load_q gave them (their angles do not depend on the slot).
+// cs(idx) returns the cos/sin of time-table entry idx.  Same arithmetic as load_q.
+template <typename CS>
+__device__ __forceinline__ void retime_q(const uint4 (&raw)[kTimeJ], int pt, int t, int hf, CS cs, bf16x8 (&qb)[8]) {
+#pragma unroll
+  for (int j = 0; j < kTimeJ; ++j) {
+    const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = 8 * j + 4 * hf + i;
+      const bool on_t = p < pt;
+      const CosSin v = cs(t * pt + (on_t ? p : 0));
+      const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xffff0000u);
+      const __bf16 r0 = (__bf16)(x0 * v.c - x1 * v.s), r1 = (__bf16)(x0 * v.s + x1 * v.c);
+      qb[j][2 * i] = on_t ? r0 : qb[j][2 * i];
+      qb[j][2 * i + 1] = on_t ? r1 : qb[j][2 * i + 1];
     }
   }
 }
@@ -188,6 +211,10 @@ void attend_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) u16 kbuf[NBUF][KB * D];
   __shared__ __attribute__((aligned(1024))) u16 vbuf[NBUF][D * KB];
   __shared__ SlotPtrs sslot[kMaxSlots];
+  // block-sparse: tile lists change slot every few blocks, so the time rotation of the queries is
+  // redone often; its cos/sin come from an LDS copy of the time table (when it fits) and the raw
+  // time part of the query stays in registers, so a slot entry waits on no global load
+  __shared__ CosSin ttab[SPARSE ? kTimeTabLds : 1];
 
   // wave index made explicitly uniform: the LDS destinations of the staging loads (M0) then stay
   // in scalar registers
@@ -210,6 +237,10 @@ void attend_bf16_kernel(AttnArgs a) {
   const RopeTab rt = a.rt;
   const int B = a.B, n_pad = a.n_pad, n_slots = a.n_slots, nt = a.nt;
   const float scale_log2 = a.scale_log2;
+  const int tt_n = rt.t_len * rt.pt;
+  const bool tt_lds = SPARSE && tt_n <= kTimeTabLds;
+  if (tt_lds)
+    for (int i = tid; i < tt_n; i += NW * 64) ttab[i] = rt.t[i];
   __syncthreads();
 
   const int nkb = (B + KB - 1) / KB;   // sparse: every slot holds B keys
@@ -259,7 +290,12 @@ void attend_bf16_kernel(AttnArgs a) {
   // instead of exp2(-inf - -inf) = NaN when another lane of the wave rescales
   float m_run = -3.0e38f, l_run = 0.f;
   bf16x8 qb[8];
-  load_q<kTimeJ, 8>(rt, qp, qvalid, qf, qh, qw, hf, 0, qb);
+  // every pair rotated once here (the first slot entry re-rotates the time pairs: retime_q keeps
+  // the others of the first kTimeJ groups as computed now)
+  load_q<0, 8>(rt, qp, qvalid, qf, qh, qw, hf, 0, qb);
+  uint4 qraw[kTimeJ];   // block-sparse: the raw time part, kept
+#pragma unroll
+  for (int j = 0; j < kTimeJ; ++j) qraw[j] = (SPARSE && qvalid) ? ldg16(qp + 16 * j + 8 * hf) : make_uint4(0, 0, 0, 0);
 
   // per-lane byte offsets of the swizzled operand reads (see stage_block)
   int koff[8], voff[4];
@@ -362,10 +398,11 @@ void attend_bf16_kernel(AttnArgs a) {
     // V^T operands of the first PV_AHEAD MFMAs are requested before the softmax, so the P.V
     // MFMAs find them in registers; MFMA i = (g, t) = (i / 4, i % 4) reads row block t, key group g
     auto vread = [&](int i) { return *reinterpret_cast<const bf16x8*>(vl + 32 * (i & 3) * KB + voff[i >> 2]); };
-    bf16x8 vop[PV_AHEAD];
+    constexpr int PVA = SPARSE ? 4 : PV_AHEAD;   // block-sparse: registers go to the kept raw query
+    bf16x8 vop[PVA];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < PV_AHEAD; ++i) vop[i] = vread(i);
+    for (int i = 0; i < PVA; ++i) vop[i] = vread(i);
     __builtin_amdgcn_sched_barrier(0);
     float mx = max_of_32(s0, s1);
     mx = swap_halves_max(mx) * scale_log2;
@@ -400,8 +437,8 @@ void attend_bf16_kernel(AttnArgs a) {
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i % PV_AHEAD], pb[i >> 2], acc[i & 3], 0, 0, 0);
-      if (i + PV_AHEAD < 16) vop[i % PV_AHEAD] = vread(i + PV_AHEAD);
+      acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i % PVA], pb[i >> 2], acc[i & 3], 0, 0, 0);
+      if (i + PVA < 16) vop[i % PVA] = vread(i + PVA);
     }
   };
   f32x16 s0, s1;
@@ -480,7 +517,16 @@ void attend_bf16_kernel(AttnArgs a) {
     sync();
     if (sl != cur_slot) {
       cur_slot = sl;
-      load_q<0, kTimeJ>(rt, qp, qvalid, qf, qh, qw, hf, sslot[sl].delta, qb);
+      const int tq = qf + sslot[sl].delta;
+      if (SPARSE) {
+        if (tt_lds) retime_q(qraw, rt.pt, tq, hf, [&](int i) { return ttab[i]; }, qb);
+        else retime_q(qraw, rt.pt, tq, hf, [&](int i) { return rt.t[i]; }, qb);
+      } else {
+        uint4 raw[kTimeJ];
+#pragma unroll
+        for (int j = 0; j < kTimeJ; ++j) raw[j] = qvalid ? ldg16(qp + 16 * j + 8 * hf) : make_uint4(0, 0, 0, 0);
+        retime_q(raw, rt.pt, tq, hf, [&](int i) { return rt.t[i]; }, qb);
+      }
     }
     qk(kbuf[cb], kvalid, afirst, s0, s1, nk, nv, kbuf[(cb + 1) % NBUF], vbuf[(cb + 1) % NBUF]);
     pend = true;
@@ -851,16 +897,19 @@ void attend_fp8_kernel(AttnArgs a) {
   // scales (E8M0 bytes) of a block: K -- the lane's key in tiles 0 and 1, shifted so that bytes 0
   // and 2 are the groups of channel chunks 0 and 1 for its half; V -- the lane's 4 channels
   auto load_scales = [&](int s, int kb, uint32_t& k0, uint32_t& k1, uint32_t& vs) {
+    // block bases uniform (scalar sums), the lane's word a 32-bit offset
     const SlotPtrs sp = sslot[s];
-    const uint8_t* kb8 = static_cast<const uint8_t*>(sp.k) + (size_t)H * kstride + (size_t)h * n_pad * 4;
-    const uint8_t* vb8 = static_cast<const uint8_t*>(sp.v) + (size_t)H * kstride + (size_t)h * n_pad * 4;
-    const uint32_t* kp = reinterpret_cast<const uint32_t*>(kb8) + kb * KB + ln;
-    k0 = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(reinterpret_cast<uintptr_t>(kp)) >>
-         (8 * hf);
-    k1 = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(reinterpret_cast<uintptr_t>(kp + 32)) >>
-         (8 * hf);
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(vb8) + (kb * 2 + hf) * 32 + ln;
-    vs = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(reinterpret_cast<uintptr_t>(vp));
+    const size_t sc0 = (size_t)H * kstride + (size_t)h * n_pad * 4;
+    const uint32_t* kp = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(uniform_ptr(sp.k)) + sc0) +
+                         (size_t)kb * KB;
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(uniform_ptr(sp.v)) + sc0) +
+                         (size_t)kb * 2 * 32;
+    auto ld = [](const uint32_t* base, uint32_t i) {
+      return *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(reinterpret_cast<uintptr_t>(base + i));
+    };
+    k0 = ld(kp, ln) >> (8 * hf);
+    k1 = ld(kp, ln + 32) >> (8 * hf);
+    vs = ld(vp, hf * 32 + ln);
   };
   auto stage = [&](int s, int kb, int buf) {
     const SlotPtrs sp = sslot[s];
