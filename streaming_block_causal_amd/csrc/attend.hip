@@ -73,6 +73,17 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// With 4-wave workgroups two of them share a CU, so each SIMD runs one wave of each and no
+// barrier ties the two together.  Each wave alternates its MFMAs and its softmax, each waiting on
+// the other's results, and the pair tends to run the same phase at the same time.  A fixed issue
+// priority for the wave in the even slot of its SIMD (HW_ID wave id, bits 3:0) lets that one run
+// ahead: about 3% faster for the block-sparse and fp8 launches (with one 8-wave workgroup per CU,
+// whose waves meet at every block's barrier, it changes nothing).
+__device__ __forceinline__ void favour_even_slot() {
+  const uint32_t slot = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 4);
+  if ((slot & 1) == 0) __builtin_amdgcn_s_setprio(1);
+}
+
 // Largest of a lane's 32 scores (two 32x32 score tiles): a tree of max3 steps, depth 4, rather
 // than a chain of 16 dependent ones.
 __device__ __forceinline__ float max_of_32(const f32x16& s0, const f32x16& s1) {
@@ -220,6 +231,7 @@ void attend_bf16_kernel(AttnArgs a) {
   // in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, ln = lane & 31;
+  if (NW == 4) favour_even_slot();   // two workgroups per CU
   // the argument struct is never addressed (that would copy it to scratch): static indices only,
   // and every field the lambdas below need is copied to a local first
 #pragma unroll
@@ -826,6 +838,7 @@ void attend_fp8_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, ln = lane & 31;
+  if (NW == 4) favour_even_slot();
 #pragma unroll
   for (int q = 0; q < kMaxSlots; ++q)
     if (tid == q) sslot[q] = a.slot[q];
