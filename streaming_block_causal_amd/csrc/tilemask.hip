@@ -18,6 +18,8 @@
 // all-pairs rank is quadratic (4096 key tiles at the largest shapes).
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace swattn {
 
 namespace {
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   __shared__ float2 xm[kQT][D / 2];
   __shared__ const float* spooled[kMaxSlots];
-  __shared__ int sdelta[kMaxSlots];
+  __shared__ CosSin relrow[kMaxSlots][32];   // each slot's time row of the relocation
 
   const int tid = threadIdx.x, qt0 = blockIdx.x * kQT, h = blockIdx.y;
   const int n_qt = min(kQT, a.nt - qt0);
@@ -65,11 +67,26 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   // the argument struct is never addressed (that would copy it to scratch): static indices only
 #pragma unroll
   for (int q = 0; q < kMaxSlots; ++q)
-    if (tid == q) {
-      spooled[q] = a.pooled[q];
-      sdelta[q] = a.delta[q];
-    }
+    if (tid == q) spooled[q] = a.pooled[q];
   const RopeTab rt = a.rt;
+  // the time rows of the relocation (step 2), one per slot, go straight into LDS now (load-to-LDS,
+  // no registers held), so their latency passes under step 1.  A row is pt <= 32 entries (256
+  // bytes, one 4-byte word per lane); lanes past its end re-read its last word, and a row of no
+  // entries reads the first word of the (back-to-back, never empty) tables: all in bounds.
+  {
+    const int w = tid >> 6, ln = tid & 63;
+    const int off = min(4 * ln, max(8 * rt.pt - 4, 0));
+    for (int sl = w; sl < a.n_slots; sl += 4) {
+      int dl = 0;
+#pragma unroll
+      for (int q = 0; q < kMaxSlots; ++q) dl = q == sl ? a.delta[q] : dl;
+      const char* row = reinterpret_cast<const char*>(rt.t + dl * rt.pt) + off;
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const __attribute__((address_space(1))) void*>(reinterpret_cast<uintptr_t>(row)),
+          reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(&relrow[sl][0])), 4, 0,
+          0);
+    }
+  }
 
   // 1. per query tile, the sum over its valid queries of q rotated at block-local positions.
   //    Thread t takes 4 pairs (16 bytes) of 8 rows (16 apart) of every tile.  Positions come from
@@ -131,6 +148,7 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
       for (int e = 0; e < 8; ++e) red[(t * 16 + rg) * D + 8 * pg + e] = acc8[e];
     }
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the relocation rows are in LDS
   __syncthreads();
   // 2. means (thread = (tile, pair)), then the relocation per slot: the time pairs are turned by
   //    delta_l; the shared array is overwritten with the relocated queries only after the barrier
@@ -150,15 +168,10 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   __syncthreads();
   for (int idx = tid; idx < n_qt * a.n_slots * (D / 2); idx += 256) {
     const int pp = idx & (D / 2 - 1), ts = idx / (D / 2), sl = ts % a.n_slots, t = ts / a.n_slots;
-    float c = 1.f, sn = 0.f;
-    if (pp < rt.pt) {
-      const CosSin v = rt.t[sdelta[sl] * rt.pt + pp];
-      c = v.c;
-      sn = v.s;
-    }
+    const CosSin v = pp < rt.pt ? relrow[sl][pp] : CosSin{1.f, 0.f};
     const float2 m = xm[t][pp];
-    qs[(t * a.n_slots + sl) * D + 2 * pp] = m.x * c - m.y * sn;
-    qs[(t * a.n_slots + sl) * D + 2 * pp + 1] = m.x * sn + m.y * c;
+    qs[(t * a.n_slots + sl) * D + 2 * pp] = m.x * v.c - m.y * v.s;
+    qs[(t * a.n_slots + sl) * D + 2 * pp + 1] = m.x * v.s + m.y * v.c;
   }
   __syncthreads();
   // 3. scores of every key tile against every query tile of the group: lane per key tile, the
@@ -205,11 +218,18 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   uint32_t kr[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) kr[c] = c < nch ? kt[64 * c + lane] : 0u;
-  auto count_ge = [&](uint32_t K) {
+  // keys >= K, for K >= 1: the register chunks past n_kv64 hold 0 and never count, so they need
+  // no branch (a uniform branch per chunk and round cost more than the compares themselves)
+  auto count_reg = [&](uint32_t K, auto NC) {
     int cnt = 0;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      if (c < nch) cnt += __popcll(__ballot(kr[c] >= K));
+    for (int c = 0; c < decltype(NC)::value; ++c) cnt += __popcll(__ballot(kr[c] >= K));
+    return cnt;
+  };
+  using C4 = std::integral_constant<int, 4>;
+  using C8 = std::integral_constant<int, 8>;
+  auto count_ge = [&](uint32_t K) {
+    int cnt = count_reg(K, C8{});
     for (int c = 8; c < nch; ++c) cnt += __popcll(__ballot(kt[64 * c + lane] >= K));
     return cnt;
   };
@@ -226,9 +246,24 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
     take_eq = 0;
   } else {
     T = 0u;
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t cand = T | (1u << b);
-      if (count_ge(cand) >= need) T = cand;
+    // every key in registers: 32 straight rounds over the chunks that can hold keys
+    if (nch <= 4) {
+#pragma unroll
+      for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        if (count_reg(cand, C4{}) >= need) T = cand;
+      }
+    } else if (nch <= 8) {
+#pragma unroll
+      for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        if (count_reg(cand, C8{}) >= need) T = cand;
+      }
+    } else {
+      for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        if (count_ge(cand) >= need) T = cand;
+      }
     }
     take_eq = need - (T == 0xffffffffu ? 0 : count_ge(T + 1u));
   }
@@ -248,9 +283,14 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
     if (keep && pos < a.k_cap) dst[pos] = u;
     count += __popcll(m);
   };
+  // chunks past n_kv64 keep nothing
+  if (nch <= 4) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    if (c < nch) emit(c, kr[c]);
+    for (int c = 0; c < 4; ++c) emit(c, kr[c]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) emit(c, kr[c]);
+  }
   for (int c = 8; c < nch; ++c) emit(c, kt[64 * c + lane]);
   for (int pos = count + lane; pos < a.k_cap; pos += 64) dst[pos] = -1;
 }
@@ -260,8 +300,8 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
 hipError_t launch_tile_mask(const Geometry& g, const RopeTab& rt, const void* q,
                             const float* const* pooled, const int* deltas, int n_slots,
                             bool has_sink, int k_row, int k_cap, int32_t* out, hipStream_t stream) {
-  if (g.d != 128 || n_slots < 1 || n_slots > kMaxSlots || n_slots * g.nt > kMaxKeyTiles)
-    return hipErrorInvalidValue;
+  if (g.d != 128 || n_slots < 1 || n_slots > kMaxSlots || n_slots * g.nt > kMaxKeyTiles || rt.pt > 32)
+    return hipErrorInvalidValue;   // (a slot's time row is staged as at most 32 entries)
   MaskArgs a;
   a.q = static_cast<const u16*>(q);
   a.out = out;
