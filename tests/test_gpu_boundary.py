@@ -162,6 +162,32 @@ def test_custom_rope_split_stream(base, split, kw):
         commit_block(c, w, n, n)
 
 
+@pytest.mark.parametrize("split, policy", [((0, 32, 32), "relative"), ((24, 20, 20), "relative"),
+                                           ((24, 20, 20), "s1")], ids=["no_time_pairs", "max_time_pairs", "max_s1"])
+def test_sparse_relocation_rows(split, policy):
+    """The tile mask stages each slot's row of the time table (pt entries, 0..24) before scoring:
+    a split with no time pairs (no relocation at all) and one with the most a bf16 cache allows,
+    against the oracle's mask and then the attention over that mask, every row."""
+    w = synth.tiny(5, name="reloc_rows", rope_split=split, n_heads=2, lat_h=16, lat_w=20, n_chunks=6,
+                   n_steps=1, sparse_keep=0.3, policy=policy)
+    n = 5                                                       # past the first eviction
+    c = _cache(w)
+    advance(c, w, n)
+    q, k, v = synth.qkv(w, n, 1)
+    c.append("current", to_dev(w, k), to_dev(w, v), n)
+    qd = to_dev(w, q)
+    _, _, kept, flips = _mask_vs_oracle(w, c, qd, n, 1, "final")
+    # attention on the oracle's mask (the GPU mask may differ at near-ties)
+    tiles = torch.tensor(np.array(kept, dtype=np.int32), device="cuda")
+    lse = torch.empty((w.n_heads, w.block_tokens), dtype=torch.float32, device="cuda")
+    out = c.attend(qd, "final", tile_idx=tiles, k_row=tiles.shape[2], lse=lse)
+    torch.cuda.synchronize()
+    ref, rl, _ = ostream.Stream(w).call(n, 1, kept=kept)
+    ok, m = compare(to_f64(out), ref, w.dtype, to_f64(lse), rl)
+    _say(f"[sparse relocation rows {split} {policy}] flips={flips} {m}")
+    assert ok, m
+
+
 def test_custom_rope_split_sparse_and_fp8():
     """The tile mask and the fp8 attention take the split too."""
     w = synth.tiny(5, name="split_sparse", rope_split=(18, 23, 23), n_heads=2, lat_h=16, lat_w=20,
