@@ -112,6 +112,9 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units: exp2 arguments stay <= 8 
 
 // Q^T operand of one wave: lane (hf, ln) holds q[row][16j + 8hf + 0..7] for j in [J0, J1), rotated
 // at time frame + delta (fp32 math, bf16 result).  Rows past the block give a zero operand.
+// Every Q load and cos/sin gather is issued before the first is used (one memory round trip, not
+// one per operand group): qp must point at a readable row -- a row past the block passes row 0's,
+// whose values a select drops -- and such a row's positions are taken as 0 (table entries exist).
 // Only the first kTimeJ operand groups hold time pairs (d = 128: 22 time pairs = dims 0..43), so a
 // new slot re-rotates those and the spatial groups are computed once per workgroup.
 constexpr int kTimeJ = 3;
@@ -119,23 +122,25 @@ constexpr int kTimeTabLds = 1024;   // time-table entries the block-sparse kerne
 template <int J0, int J1>
 __device__ __forceinline__ void load_q(const RopeTab rt, const u16* qp, bool valid, int qf, int qh, int qw,
                                        int hf, int delta, bf16x8 (&qb)[8]) {
-  const int t = qf + delta;
+  constexpr int NJ = J1 - J0;
+  const int t = valid ? qf + delta : 0, ph = valid ? qh : 0, pw = valid ? qw : 0;
+  uint4 raw[NJ];
+  float c[NJ][4], s[NJ][4];
 #pragma unroll
-  for (int j = J0; j < J1; ++j) {
-    if (!valid) {
+  for (int j = 0; j < NJ; ++j) raw[j] = ldg16(qp + 16 * (J0 + j) + 8 * hf);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qb[j][i] = (__bf16)0.f;
-      continue;
-    }
-    const uint4 raw = ldg16(qp + 16 * j + 8 * hf);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rope_cs(rt, 8 * (J0 + j) + 4 * hf + i, t, ph, pw, c[j][i], s[j][i]);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float c, s;
-      rope_cs(rt, 8 * j + 4 * hf + i, t, qh, qw, c, s);
-      const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xffff0000u);
-      qb[j][2 * i] = (__bf16)(x0 * c - x1 * s);
-      qb[j][2 * i + 1] = (__bf16)(x0 * s + x1 * c);
+      const float x0 = valid ? __uint_as_float(w[i] << 16) : 0.f;
+      const float x1 = valid ? __uint_as_float(w[i] & 0xffff0000u) : 0.f;
+      qb[J0 + j][2 * i] = (__bf16)(x0 * c[j][i] - x1 * s[j][i]);
+      qb[J0 + j][2 * i + 1] = (__bf16)(x0 * s[j][i] + x1 * c[j][i]);
     }
   }
 }
@@ -284,7 +289,8 @@ void attend_bf16_kernel(AttnArgs a) {
   const int qf = qrow / a.hw;
   const int qrem = qrow - qf * a.hw;
   const int qh = qrem / a.lat_w, qw = qrem - qh * a.lat_w;
-  const u16* qp = static_cast<const u16*>(a.q) + ((size_t)qrow * a.H + h) * D;
+  // a row past the block reads row 0 (its values are dropped): every query load is in bounds
+  const u16* qp = static_cast<const u16*>(a.q) + ((size_t)(qvalid ? qrow : 0) * a.H + h) * D;
   // frame of key j = floor((j + 0.5) / hw) in fp32: exact, since j < 65536 keeps the rounding error
   // below 0.01 / hw while (j + 0.5) / hw is at least 0.5 / hw from an integer.  A kernel argument,
   // so it stays in a scalar register: a value computed here would live in a vector register, be
@@ -307,7 +313,10 @@ void attend_bf16_kernel(AttnArgs a) {
   load_q<0, 8>(rt, qp, qvalid, qf, qh, qw, hf, 0, qb);
   uint4 qraw[kTimeJ];   // block-sparse: the raw time part, kept
 #pragma unroll
-  for (int j = 0; j < kTimeJ; ++j) qraw[j] = (SPARSE && qvalid) ? ldg16(qp + 16 * j + 8 * hf) : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < kTimeJ; ++j) {   // (a load for every row, then a select: no branch, no wait between)
+    const uint4 r = SPARSE ? ldg16(qp + 16 * j + 8 * hf) : make_uint4(0, 0, 0, 0);
+    qraw[j] = qvalid ? r : make_uint4(0, 0, 0, 0);
+  }
 
   // per-lane byte offsets of the swizzled operand reads (see stage_block)
   int koff[8], voff[4];
