@@ -197,14 +197,23 @@ def _run_sparse(w, n, s, heads):
     return c, q, idx, k_row, kept
 
 
-def test_tile_mask_many_key_tiles():
+@pytest.mark.parametrize("shape", ["640", "376"])
+def test_tile_mask_many_key_tiles(shape):
     """640 key tiles per query tile (2 frames of 64 x 64 latents = 64 tiles a block; a sink, 8
     window blocks and the current one): the selection walks a score table larger than the 512
-    entries a wave holds in registers."""
-    w = synth.tiny(5, name="mask_wide", frames=2, lat_h=64, lat_w=64, n_heads=2, n_sink=1, n_window=8,
-                   n_chunks=10, n_steps=1, sparse_keep=0.1)
-    assert (w.n_sink + w.n_window + 1) * otm.n_tiles(w.block_tokens) == 640
-    _run_sparse(w, 9, 1, heads=[0, 1])
+    entries a wave holds in registers.  376 key tiles (3 frames of 40 x 50 = 6000 tokens, 47 tiles
+    a block with a ragged last one; a sink, 6 window blocks and the current one): six of the eight
+    register chunks, the last one partly past the end of the table."""
+    if shape == "640":
+        w = synth.tiny(5, name="mask_wide", frames=2, lat_h=64, lat_w=64, n_heads=2, n_sink=1, n_window=8,
+                       n_chunks=10, n_steps=1, sparse_keep=0.1)
+        n, n_kv = 9, 640
+    else:
+        w = synth.tiny(5, name="mask_mid", frames=3, lat_h=40, lat_w=50, n_heads=2, n_sink=1, n_window=6,
+                       n_chunks=8, n_steps=1, sparse_keep=0.1)
+        n, n_kv = 7, 376
+    assert (w.n_sink + w.n_window + 1) * otm.n_tiles(w.block_tokens) == n_kv
+    _run_sparse(w, n, 1, heads=[0, 1])
 
 
 def test_tile_mask_ties_go_to_lower_index():
