@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256) void tile_mask_kernel(MaskArgs a) {
   // bytes, one 4-byte word per lane); lanes past its end re-read its last word, and a row of no
   // entries reads the first word of the (back-to-back, never empty) tables: all in bounds.
   {
-    const int w = tid >> 6, ln = tid & 63;
+    // the wave index made uniform: slot loop, delta and LDS row address stay scalar
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), ln = tid & 63;
     const int off = min(4 * ln, max(8 * rt.pt - 4, 0));
     for (int sl = w; sl < a.n_slots; sl += 4) {
       int dl = 0;
